@@ -1,0 +1,243 @@
+"""Benchmark: achieved HBM GB/s of the streaming row sum and the int8 dequant dot on one MI355X.
+
+One step is one pass of the whole hot path over resident synthetic inputs:
+  1. row_sums        65536 x 4096 f32                        (1,074,003,968 B)
+  2. i8_dequant_dot  16384 x 8192 int8 weights, 1 vector      (134,356,992 B, v_dot4)
+  3. i8_dequant_dot  28672 x 8192 int8 weights, 8 vectors     (235,978,784 B, MFMA)
+Bytes are algorithmic (each input read once, each output written once).  The
+1 GiB row-sum stream between consecutive int8 launches evicts their weights from
+the 256 MB last-level cache, so every launch reads HBM.
+
+Prints one JSON line.  `value` is total algorithmic bytes per step / time per
+step.  `roofline` is for the dominant kernel (row_sums): its algorithmic bytes
+/ its mean duration from HIP events on the launch stream.  `cpu_baseline` is
+the CPU oracle on the same workload (also used to check the outputs).
+
+  python bench.py [--steps K] [--warmup W] [--segments] [--calibrate-copy MiB]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (and % of peak) for row-sum and int8 dequant-dot"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_sums_65536x4096.json")
+KERNEL_SOURCES = ("device_common.hpp", "internal.hpp", "row_sums.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "int8_dequant_dot_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--segments", action="store_true", help="also time segment_sums on 16384 segments")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run loom_copy_f32 over MIB MiB (counter calibration) and exit")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(every workload shards by independent rows; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int8_dequant_dot_amd as loom
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, device=dev)
+        b = torch.empty(n, device=dev)
+        for _ in range(5):
+            loom.copy_f32(a, b)
+        torch.cuda.synchronize()
+        log(f"copy_f32 calibration: {n} floats ({4 * n} B read, {4 * n} B written) x 5")
+        return
+
+    # ---------------------------------------------------------------- inputs (resident in HBM)
+    t0 = time.time()
+    R2, C2 = 65536, 4096
+    x2 = synth.dense_matrix(synth.DENSE.seed, R2, C2, device=dev)
+    out2 = torch.empty(R2, device=dev)
+
+    R4, K4 = 16384, 8192
+    w4 = synth.i8_matrix(synth.GEMV.seed, synth.S_W, R4, K4, device=dev)
+    x4 = synth.i8_matrix(synth.GEMV.seed, synth.S_X, 1, K4, device=dev)
+    s4 = synth.scales(synth.GEMV.seed, synth.S_WSCALE, 0, R4, device=dev)
+    out4 = torch.empty(R4, 1, device=dev)
+
+    R5, K5, B5 = 28672, 8192, 8
+    w5 = synth.i8_matrix(synth.BATCHED.seed, synth.S_W, R5, K5, device=dev)
+    x5 = synth.i8_matrix(synth.BATCHED.seed, synth.S_X, B5, K5, device=dev)
+    s5 = synth.scales(synth.BATCHED.seed, synth.S_WSCALE, 0, R5, device=dev)
+    sx5 = synth.scales(synth.BATCHED.seed, synth.S_XSCALE, 0, B5, device=dev)
+    out5 = torch.empty(R5, B5, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    w4p, x4p, w5p, x5p = loom.pack_int8(w4), loom.pack_int8(x4), loom.pack_int8(w5), loom.pack_int8(x5)
+    bytes2 = R2 * C2 * 4 + R2 * 4
+    bytes4 = R4 * K4 + K4 + R4 * 4 + R4 * 4
+    bytes5 = R5 * K5 + B5 * K5 + R5 * 4 + B5 * 4 + R5 * B5 * 4
+    step_bytes = bytes2 + bytes4 + bytes5
+
+    kernels = [
+        ("row_sums", bytes2, lambda: loom.row_sums(x2, out2)),
+        ("i8_dequant_dot_gemv", bytes4, lambda: loom.i8_dequant_dot(w4p, s4, x4p, None, out=out4)),
+        ("i8_dequant_dot_batched", bytes5, lambda: loom.i8_dequant_dot(w5p, s5, x5p, sx5, out=out5)),
+    ]
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for _, _, fn in kernels:
+            fn()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in kernels]
+          for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(K):
+        for j, (_, _, fn) in enumerate(kernels):
+            ev[s][j][0].record(stream)
+            fn()
+            ev[s][j][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    per_kernel_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(K)]))
+                     for j in range(len(kernels))]
+    log(f"timed {K} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    parts = {}
+    for (name, nbytes, _), ms in zip(kernels, per_kernel_ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        parts[name] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                       "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    if args.segments:
+        S, CS = 16384, 256
+        L = synth.segment_lengths(synth.SEGMENTS.seed, S, 4096, device=dev)
+        off = synth.segment_offsets(L)
+        total = int(off[-1].item())
+        x3 = synth.segment_matrix(synth.SEGMENTS.seed, total, CS, device=dev)
+        out3 = torch.empty(S, CS, device=dev)
+        t3 = torch.empty(S, dtype=torch.int32, device=dev)
+        bytes3 = total * CS * 4 + (S + 1) * 8 + S * CS * 4 + S * 4
+        for _ in range(2):
+            loom.segment_sums(x3, off, out3, t3)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(3, K // 4)
+        e0.record(stream)
+        for _ in range(reps):
+            loom.segment_sums(x3, off, out3, t3)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms3 = e0.elapsed_time(e1) / reps
+        gbs3 = bytes3 / (ms3 * 1e-3) / 1e9
+        parts["segment_sums"] = {"bytes": bytes3, "us": round(ms3 * 1e3, 1), "GB/s": round(gbs3, 1),
+                                 "frac_of_peak": round(gbs3 / HBM_PEAK_GBS, 4), "rows": total}
+        del x3
+        torch.cuda.empty_cache()
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- roofline of the dominant kernel
+    achieved = parts["row_sums"]["GB/s"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "row_sums 65536x4096 f32", "algorithmic_bytes": bytes2}
+
+    # ---------------------------------------------------------------- CPU oracle baseline (+ output check)
+    cpu = None
+    check = None
+    if not args.no_cpu:
+        import oracle
+        hx2, hw4, hx4, hs4 = x2.cpu().numpy(), w4.cpu().numpy(), x4.cpu().numpy(), s4.cpu().numpy()
+        hw5, hx5, hs5, hsx5 = w5.cpu().numpy(), x5.cpu().numpy(), s5.cpu().numpy(), sx5.cpu().numpy()
+        passes, t_cpu = 0, 0.0
+        while passes == 0 or t_cpu < 10.0:
+            t = time.perf_counter()
+            r2, _, a2 = oracle.row_sums(hx2, shadows=(passes == 0))
+            r4, acc4 = oracle.i8_dequant_dot(hw4, hs4, hx4)
+            r5, acc5 = oracle.i8_dequant_dot(hw5, hs5, hx5, hsx5)
+            t_cpu += time.perf_counter() - t
+            passes += 1
+            if passes == 1:
+                g2, g4, g5 = out2.cpu().numpy(), out4.cpu().numpy(), out5.cpu().numpy()
+                err2 = float(np.max(np.abs(g2.astype(np.float64) - r2) / a2))
+                err4 = float(np.max(np.abs(g4.astype(np.float64) - r4) / np.abs(r4)))
+                err5 = float(np.max(np.abs(g5.astype(np.float64) - r5) / np.abs(r5)))
+                check = {"row_sums_max_err_over_sum_abs": err2, "gemv_max_rel_err": err4,
+                         "batched_max_rel_err": err5,
+                         "pass": bool(err2 <= 1e-5 and err4 <= 2e-5 and err5 <= 2e-5)}
+                log(f"oracle check: {check}")
+        cpu_gbs = passes * step_bytes / t_cpu / 1e9
+        cpu = {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the full step (all three kernels' inputs and outputs), {passes} pass(es), "
+                         f"{t_cpu:.1f}s, single-threaded C oracle"}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+int8(int32 acc)",
+        "data": "synthetic (seeded SplitMix64, generated on the GPU)",
+        "config": {"workload": "row_sums 65536x4096 f32 + i8_dequant_dot 16384x8192x1 + 28672x8192x8",
+                   "bytes_per_step": step_bytes, "frac_of_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parts": parts,
+        "oracle_check": check,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

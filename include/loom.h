@@ -1,0 +1,190 @@
+/*
+ * loom.h -- C ABI of the MI355X (gfx950, CDNA4) streaming-reduction library.
+ *
+ * The library computes the data-parallel hot path described by the Loom pages
+ * "Tune loop unrolling and pipelining" (TUNE), "Functions and structured
+ * control flow" (CTRL) and "Kernels and launch configuration" (LAUNCH): a
+ * streaming reduction over records in memory -- row-tiled f32 sums with a
+ * subgroup (wave64) reduction per row, full 8-row tiles with a separate ragged
+ * tail, read-ahead of the next records -- and its extension to packed
+ * signed-byte (int8) dequantization with dot accumulation.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Return LOOM_OK (0) or a negative loom_status.  All argument checks run on
+ *    the host before anything is enqueued; on error nothing is launched and no
+ *    output is touched.
+ *  - Data pointers are device pointers (HIP allocations of the current device,
+ *    e.g. a torch tensor's data_ptr()).  The caller owns all memory.  The
+ *    library allocates no device memory and keeps no pointer after returning.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously on it; outputs are ready once the stream has reached the
+ *    enqueued work.  A device-side fault is reported by later HIP calls, not
+ *    by the return code; LOOM_ERR_DEVICE means the launch itself was refused.
+ *  - Calls are thread-safe: the only shared state is an immutable table.
+ *  - Matrices are row-major.  Packed int8: an int32 word j of a row holds the
+ *    elements 4j..4j+3, element 4j+b in byte b (little-endian), two's
+ *    complement -- exactly the bytes of an int8 array viewed as int32.
+ */
+#ifndef LOOM_H
+#define LOOM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum loom_status {
+    LOOM_OK = 0,
+    LOOM_ERR_NULL = -1,           /* a required pointer is NULL                          */
+    LOOM_ERR_RANGE = -2,          /* a size or count outside its documented range        */
+    LOOM_ERR_ALIGN = -3,          /* a pointer or stride not aligned as documented       */
+    LOOM_ERR_SHAPE = -4,          /* inconsistent shape (e.g. k not a multiple of 4)     */
+    LOOM_ERR_UNKNOWN_EXPORT = -5, /* no kernel exports this name                         */
+    LOOM_ERR_TOKEN = -6,          /* invalid launch-config token or workload arity       */
+    LOOM_ERR_DEVICE = -7          /* the HIP runtime refused the launch                  */
+} loom_status;
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *loom_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int loom_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * Launch configuration (LAUNCH §A kernel owns two signatures, §Workload is  *
+ * not workgroup count, §Evaluate the compiled launch contract).             *
+ *                                                                           *
+ * Each kernel owns the mapping from its logical workload (element, row or   *
+ * segment counts) to a physical grid.  An embedding resolves an export name  *
+ * to a token once, then evaluates the geometry for any workload without     *
+ * compiling anything.  The entry points below use the same evaluation, so   *
+ * the host never duplicates the grid arithmetic.                            *
+ * ------------------------------------------------------------------------ */
+typedef struct loom_launch_config {
+    uint32_t workgroups[3];          /* grid, in workgroups                       */
+    uint32_t workgroup_size[3];      /* work-items per workgroup                  */
+    uint32_t cluster_size[3];        /* always {1,1,1}: gfx950 has no clusters    */
+    uint32_t subgroup_size;          /* 64: gfx950 waves are 64 wide              */
+    uint32_t workgroup_storage_bytes;/* LDS the kernel needs per workgroup        */
+} loom_launch_config;
+
+/* Export names and their workload signatures (each an int64 passed as its
+ * uint64 bit pattern):
+ *   "copy_f32"        (n)
+ *   "row_sum_tiles"   (count)
+ *   "row_sums"        (rows, cols)
+ *   "segment_sums"    (segments, cols)
+ *   "i8_dequant_dot"  (rows, k, batch)
+ * lookup: LOOM_ERR_NULL if a pointer is NULL, LOOM_ERR_UNKNOWN_EXPORT if no
+ * kernel has that name.  The token stays valid for the life of the process. */
+int loom_launch_config_lookup(const char *export_name, uint32_t *token);
+
+/* Evaluates the launch configuration of `token` for the given workload.
+ * Pure host arithmetic; no device call.  LOOM_ERR_TOKEN for an unknown token
+ * or a workload_count that differs from the export's arity, LOOM_ERR_RANGE
+ * for a negative workload value or a grid beyond the hardware limits.
+ * A workload with nothing to do yields workgroups {0,1,1}. */
+int loom_launch_config_invoke(uint32_t token, const uint64_t *workload_bits,
+                              size_t workload_count, loom_launch_config *out);
+
+/* ------------------------------------------------------------------------ *
+ * Guarded over-dispatched copy (LAUNCH §Over-dispatch safely and preserve   *
+ * the proof).  out[i] = in[i] for 0 <= i < n, on ceil(n/256) workgroups of   *
+ * 256 work-items; work-items at or beyond n touch nothing, so out[n..] is   *
+ * left as it was (1009 elements run on 4 workgroups).                       *
+ *   in, out : f32[n], device, 4-byte aligned; may be NULL only when n == 0  *
+ *   n       : 0 <= n <= 2^31 * 255 (LOOM_ERR_RANGE otherwise)               *
+ * ------------------------------------------------------------------------ */
+int loom_copy_f32(const float *in, float *out, int64_t n, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * Tiled row sum of one 32-lane tile (TUNE §Derive full tiles from a ragged  *
+ * loop, @guide.sum_full_tiles).  For lane l < 32:                           *
+ *     sums[l] = initial[l] + sum over rows r < final_row of rowsum(r)       *
+ * where rowsum(r) is the subgroup reduction of values[r][0..31], rows are   *
+ * taken in full tiles of 8 in row order, final_row = 8*floor(count/8) and   *
+ * tail_count = count mod 8.  The tail rows [final_row, count) are NOT       *
+ * summed and NOT read: they are returned for a separate cleanup.            *
+ *   values     : f32[rows_alloc][32], device, 4-byte aligned                *
+ *   rows_alloc : rows allocated, 0 <= rows_alloc <= 2^26                    *
+ *   count      : logical row count, 0 <= count <= rows_alloc (the page's    *
+ *                inclusive range assumption, checked: LOOM_ERR_RANGE)       *
+ *   initial    : f32[32] per-lane start value, or NULL for 0.0              *
+ *   sums       : f32[32] output                                             *
+ *   final_row, tail_count : int32[1] outputs, device                        *
+ * ------------------------------------------------------------------------ */
+int loom_row_sum_tiles(const float *values, int64_t rows_alloc, int64_t count,
+                       const float *initial, float *sums, int32_t *final_row,
+                       int32_t *tail_count, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * Streaming row sums (TUNE §Derive full tiles, §Give each motif its own     *
+ * schedule, §Read-ahead; CTRL §Pipeline reads ahead of ordered computation) *
+ *     out[r] = sum_{c < cols} x[r*row_stride + c],   0 <= r < rows          *
+ * Rows are processed in full 8-row tiles plus one guarded tail tile; each   *
+ * row is streamed with coalesced loads read ahead of the accumulation and   *
+ * finished by a wave64 reduction.  f32 accumulation; the summation order    *
+ * inside a row is a tree (error <= 1e-5 * sum|x| for the documented sizes). *
+ *   x          : f32, device, 4-byte aligned (16-byte alignment of x and    *
+ *                row_stride % 4 == 0 select 128-bit loads)                  *
+ *   rows, cols : 0 <= rows < 2^31, 0 <= cols < 2^31                         *
+ *   row_stride : elements between row starts, row_stride >= cols            *
+ *   out        : f32[rows], device                                          *
+ * ------------------------------------------------------------------------ */
+int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t row_stride,
+                  float *out, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * Per-segment column sums (TUNE §Keep one checked source for experiments:   *
+ * each lane sums its column over the rows, in row order; §Derive full       *
+ * tiles: full 8-row tiles then the tail).                                   *
+ *     out[s][c] = sum_{offsets[s] <= r < offsets[s+1]} x[r][c]              *
+ *     tail_counts[s] = (offsets[s+1] - offsets[s]) mod 8                    *
+ * Each column accumulates its rows in row order in f32, so every output is  *
+ * the in-order recurrence (an empty segment gives +0.0).                    *
+ *   x           : f32[total_rows][cols], device, row-major, 4-byte aligned  *
+ *   total_rows  : rows in x, 0 <= total_rows < 2^40                         *
+ *   offsets     : int64[segments+1], device, CSR row offsets.  A segment    *
+ *                 with offsets[s] > offsets[s+1], offsets[s] < 0 or         *
+ *                 offsets[s+1] > total_rows reads nothing; its outputs are  *
+ *                 set to NaN and its tail count to -1.                      *
+ *   segments    : 0 <= segments < 2^31                                      *
+ *   cols        : 0 <= cols <= 2^20                                         *
+ *   out         : f32[segments][cols], device                               *
+ *   tail_counts : int32[segments], device, or NULL                          *
+ * ------------------------------------------------------------------------ */
+int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets,
+                      int64_t segments, int64_t cols, float *out,
+                      int32_t *tail_counts, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * Packed signed-byte dequantization with dot accumulation (TUNE §Apply the  *
+ * same controls to a packed dot product; scales factored out of the sum).   *
+ *     acc[r][b] = sum_{i < k} w[r][i] * x[b][i]          (exact, int32)     *
+ *     out[r][b] = (f32(acc[r][b]) * w_scale[r]) * x_scale[b]                *
+ * with each product rounded once to f32; when x_scale is NULL the second    *
+ * product is skipped.  batch == 1 runs a v_dot4 (int8x4) GEMV; batch >= 2   *
+ * runs an int8 MFMA kernel.                                                 *
+ *   w       : int32[rows][k/4] packed int8 weights, device, 4-byte aligned  *
+ *   w_scale : f32[rows], device                                             *
+ *   x       : int32[batch][k/4] packed int8 activations, device             *
+ *   x_scale : f32[batch], device, or NULL (= 1)                             *
+ *   rows    : 0 <= rows < 2^31                                              *
+ *   k       : elements per row, k % 4 == 0 (LOOM_ERR_SHAPE), 0 <= k <=      *
+ *             131068 so |acc| <= 2^31 - 1 (LOOM_ERR_RANGE)                  *
+ *   batch   : 1 <= batch <= 64 (LOOM_ERR_RANGE)                             *
+ *   out     : f32[rows][batch], device                                      *
+ *   acc     : int32[rows][batch], device, or NULL (not written)             *
+ * ------------------------------------------------------------------------ */
+int loom_i8_dequant_dot(const int32_t *w, const float *w_scale, const int32_t *x,
+                        const float *x_scale, int64_t rows, int64_t k, int64_t batch,
+                        float *out, int32_t *acc, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOM_H */

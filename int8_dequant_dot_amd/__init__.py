@@ -1,0 +1,201 @@
+"""Python binding of the MI355X streaming-reduction library (``libloom.so``).
+
+Argument marshalling only: every step of the computation runs in the gfx950 HIP
+kernels behind the C ABI declared in ``include/loom.h``.  PyTorch supplies device
+memory and the stream (``torch.cuda.current_stream()``).  There is no CPU
+fallback: if the HIP library is missing, importing this package raises.
+
+Functions carry the C entry points' names without the ``loom_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # load torch's HIP runtime first so libloom.so binds to the same instance
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libloom.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib.loom_status_string.restype = ctypes.c_char_p
+_lib.loom_status_string.argtypes = [ctypes.c_int]
+_lib.loom_version.restype = ctypes.c_int
+_lib.loom_version.argtypes = []
+_lib.loom_launch_config_lookup.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_uint32)]
+_lib.loom_launch_config_invoke.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint64), ctypes.c_size_t, _p]
+_lib.loom_copy_f32.argtypes = [_p, _p, _i64, _p]
+_lib.loom_row_sum_tiles.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _p]
+_lib.loom_row_sums.argtypes = [_p, _i64, _i64, _i64, _p, _p]
+_lib.loom_segment_sums.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p, _p]
+_lib.loom_i8_dequant_dot.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p]
+for _name in ("loom_launch_config_lookup", "loom_launch_config_invoke", "loom_copy_f32", "loom_row_sum_tiles",
+              "loom_row_sums", "loom_segment_sums", "loom_i8_dequant_dot"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+# status codes (include/loom.h)
+OK, ERR_NULL, ERR_RANGE, ERR_ALIGN, ERR_SHAPE, ERR_UNKNOWN_EXPORT, ERR_TOKEN, ERR_DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
+
+EXPORTS = ("copy_f32", "row_sum_tiles", "row_sums", "segment_sums", "i8_dequant_dot")
+
+
+class LoomError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class LaunchConfig(ctypes.Structure):
+    _fields_ = [("workgroups", ctypes.c_uint32 * 3), ("workgroup_size", ctypes.c_uint32 * 3),
+                ("cluster_size", ctypes.c_uint32 * 3), ("subgroup_size", ctypes.c_uint32),
+                ("workgroup_storage_bytes", ctypes.c_uint32)]
+
+    def as_dict(self):
+        return {"workgroups": tuple(self.workgroups), "workgroup_size": tuple(self.workgroup_size),
+                "cluster_size": tuple(self.cluster_size), "subgroup_size": self.subgroup_size,
+                "workgroup_storage_bytes": self.workgroup_storage_bytes}
+
+
+def library():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.loom_status_string(status).decode()
+
+
+def version() -> int:
+    return _lib.loom_version()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise LoomError(status, where)
+
+
+def launch_config_lookup(export_name: str) -> int:
+    tok = ctypes.c_uint32()
+    _check(_lib.loom_launch_config_lookup(export_name.encode(), ctypes.byref(tok)), "launch_config_lookup")
+    return tok.value
+
+
+def launch_config_invoke(token: int, workload) -> dict:
+    vals = [int(v) & ((1 << 64) - 1) for v in workload]
+    arr = (ctypes.c_uint64 * max(1, len(vals)))(*vals)
+    cfg = LaunchConfig()
+    _check(_lib.loom_launch_config_invoke(token, arr, len(vals), ctypes.byref(cfg)), "launch_config_invoke")
+    return cfg.as_dict()
+
+
+# ------------------------------------------------------------------ tensor helpers
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def copy_f32(inp: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out[i] = inp[i] for i < inp.numel(); elements of ``out`` beyond that are untouched."""
+    _dev(inp, torch.float32, "inp")
+    assert inp.is_contiguous()
+    if out is None:
+        out = torch.empty_like(inp)
+    _dev(out, torch.float32, "out")
+    assert out.is_contiguous() and out.numel() >= inp.numel()
+    _check(_lib.loom_copy_f32(_ptr(inp), _ptr(out), inp.numel(), _stream(inp)), "copy_f32")
+    return out
+
+
+def row_sum_tiles(values: torch.Tensor, count: int, initial: torch.Tensor | None = None):
+    """values [rows_alloc][32] f32 -> (sums[32] f32, final_row int32[1], tail_count int32[1])."""
+    _dev(values, torch.float32, "values")
+    assert values.dim() == 2 and values.shape[1] == 32 and values.is_contiguous()
+    if initial is not None:
+        _dev(initial, torch.float32, "initial")
+        assert initial.numel() == 32 and initial.is_contiguous()
+    sums = torch.empty(32, dtype=torch.float32, device=values.device)
+    fr = torch.empty(1, dtype=torch.int32, device=values.device)
+    tc = torch.empty(1, dtype=torch.int32, device=values.device)
+    _check(_lib.loom_row_sum_tiles(_ptr(values), values.shape[0], count, _ptr(initial), _ptr(sums), _ptr(fr),
+                                   _ptr(tc), _stream(values)), "row_sum_tiles")
+    return sums, fr, tc
+
+
+def row_sums(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """x [rows][cols] f32 with unit column stride (any row stride) -> out [rows]."""
+    _dev(x, torch.float32, "x")
+    assert x.dim() == 2 and (x.stride(1) == 1 or x.shape[1] <= 1)
+    rows, cols = x.shape
+    stride = x.stride(0) if rows > 1 else max(cols, 1)
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    _check(_lib.loom_row_sums(_ptr(x), rows, cols, stride, _ptr(out), _stream(x)), "row_sums")
+    return out
+
+
+def segment_sums(x: torch.Tensor, offsets: torch.Tensor, out: torch.Tensor | None = None,
+                 tail_counts: torch.Tensor | None = None, want_tails: bool = True):
+    """x [total_rows][cols] f32, offsets int64 [S+1] (CSR) -> (out [S][cols], tail_counts int32 [S])."""
+    _dev(x, torch.float32, "x")
+    _dev(offsets, torch.int64, "offsets")
+    assert x.dim() == 2 and x.is_contiguous() and offsets.dim() == 1 and offsets.is_contiguous()
+    S = offsets.numel() - 1
+    cols = x.shape[1]
+    if out is None:
+        out = torch.empty(S, cols, dtype=torch.float32, device=x.device)
+    if tail_counts is None and want_tails:
+        tail_counts = torch.empty(S, dtype=torch.int32, device=x.device)
+    _check(_lib.loom_segment_sums(_ptr(x), x.shape[0], _ptr(offsets), S, cols, _ptr(out), _ptr(tail_counts),
+                                  _stream(x)), "segment_sums")
+    return out, tail_counts
+
+
+def i8_dequant_dot(w: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, x_scale: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None, acc: torch.Tensor | None = None, want_acc: bool = False):
+    """w int32 [rows][k/4] (packed int8), x int32 [batch][k/4] or [k/4] -> out f32 [rows][batch] (and acc)."""
+    _dev(w, torch.int32, "w")
+    _dev(x, torch.int32, "x")
+    _dev(w_scale, torch.float32, "w_scale")
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    assert w.dim() == 2 and w.is_contiguous() and x.is_contiguous() and x.shape[1] == w.shape[1]
+    rows, kw = w.shape
+    batch = x.shape[0]
+    if x_scale is not None:
+        _dev(x_scale, torch.float32, "x_scale")
+    if out is None:
+        out = torch.empty(rows, batch, dtype=torch.float32, device=w.device)
+    if acc is None and want_acc:
+        acc = torch.empty(rows, batch, dtype=torch.int32, device=w.device)
+    _check(_lib.loom_i8_dequant_dot(_ptr(w), _ptr(w_scale), _ptr(x), _ptr(x_scale), rows, 4 * kw, batch,
+                                    _ptr(out), _ptr(acc), _stream(w)), "i8_dequant_dot")
+    return (out, acc) if want_acc else out
+
+
+def pack_int8(t: torch.Tensor) -> torch.Tensor:
+    """View an int8 [..., k] tensor (k % 4 == 0) as packed int32 [..., k/4] words (no copy)."""
+    assert t.dtype == torch.int8 and t.shape[-1] % 4 == 0 and t.is_contiguous()
+    if t.shape[-1] == 0:
+        return torch.empty(*t.shape[:-1], 0, dtype=torch.int32, device=t.device)
+    return t.view(torch.int32)

@@ -1,0 +1,112 @@
+// abi.cpp -- the extern "C" entry points declared in include/loom.h.
+//
+// Every entry point validates its arguments on the host (sizes, then
+// pointers, then alignment), evaluates its kernel's launch configuration
+// through the same table embeddings use, and enqueues the kernel on the
+// caller's stream.  Nothing is launched when there is nothing to compute or
+// when a check fails.
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace {
+
+bool misaligned(const void *p, uintptr_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? LOOM_OK : LOOM_ERR_DEVICE; }
+
+constexpr int64_t kMaxRows = 0x7FFFFFFF;        // row / segment counts index a 1-D grid
+constexpr int64_t kMaxTileRows = int64_t(1) << 26;
+constexpr int64_t kMaxTotalRows = int64_t(1) << 40;
+constexpr int64_t kMaxSegmentCols = int64_t(1) << 20;
+constexpr int64_t kMaxCopy = int64_t(0x7FFFFFFF) * 255;
+
+}  // namespace
+
+extern "C" const char *loom_status_string(int status) {
+    switch (status) {
+        case LOOM_OK: return "ok";
+        case LOOM_ERR_NULL: return "a required pointer is NULL";
+        case LOOM_ERR_RANGE: return "a size or count is outside its documented range";
+        case LOOM_ERR_ALIGN: return "a pointer or stride is not aligned as documented";
+        case LOOM_ERR_SHAPE: return "inconsistent shape";
+        case LOOM_ERR_UNKNOWN_EXPORT: return "no kernel exports this name";
+        case LOOM_ERR_TOKEN: return "invalid launch-config token or workload arity";
+        case LOOM_ERR_DEVICE: return "the HIP runtime refused the launch";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int loom_version(void) { return 100; }
+
+extern "C" int loom_copy_f32(const float *in, float *out, int64_t n, void *stream) {
+    if (n < 0 || n > kMaxCopy) return LOOM_ERR_RANGE;
+    if (n == 0) return LOOM_OK;
+    if (!in || !out) return LOOM_ERR_NULL;
+    if (misaligned(in, 4) || misaligned(out, 4)) return LOOM_ERR_ALIGN;
+    loom_launch_config cfg;
+    const int64_t w[1] = {n};
+    if (int st = loom::evaluate_launch(loom::kCopyF32, w, &cfg)) return st;
+    return launch_status(loom::launch_copy_f32(cfg, in, out, n, (hipStream_t)stream));
+}
+
+extern "C" int loom_row_sum_tiles(const float *values, int64_t rows_alloc, int64_t count, const float *initial,
+                                  float *sums, int32_t *final_row, int32_t *tail_count, void *stream) {
+    if (rows_alloc < 0 || rows_alloc > kMaxTileRows || count < 0 || count > rows_alloc) return LOOM_ERR_RANGE;
+    if (!sums || !final_row || !tail_count || (!values && rows_alloc > 0)) return LOOM_ERR_NULL;
+    if (misaligned(values, 4) || misaligned(initial, 4) || misaligned(sums, 4) || misaligned(final_row, 4) ||
+        misaligned(tail_count, 4))
+        return LOOM_ERR_ALIGN;
+    loom_launch_config cfg;
+    const int64_t w[1] = {count};
+    if (int st = loom::evaluate_launch(loom::kRowSumTiles, w, &cfg)) return st;
+    return launch_status(loom::launch_row_sum_tiles(cfg, values, (int)count, initial, sums, final_row, tail_count,
+                                                    (hipStream_t)stream));
+}
+
+extern "C" int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t row_stride, float *out,
+                             void *stream) {
+    if (rows < 0 || rows > kMaxRows || cols < 0 || cols > kMaxRows) return LOOM_ERR_RANGE;
+    if (row_stride < cols) return LOOM_ERR_SHAPE;
+    if (rows > 0 && row_stride > (INT64_MAX / 4) / rows) return LOOM_ERR_RANGE;
+    if (rows == 0) return LOOM_OK;
+    if (!out || (!x && cols > 0)) return LOOM_ERR_NULL;
+    if (misaligned(x, 4) || misaligned(out, 4)) return LOOM_ERR_ALIGN;
+    loom_launch_config cfg;
+    const int64_t w[2] = {rows, cols};
+    if (int st = loom::evaluate_launch(loom::kRowSums, w, &cfg)) return st;
+    return launch_status(loom::launch_row_sums(cfg, x, (int)rows, (int)cols, row_stride, out, (hipStream_t)stream));
+}
+
+extern "C" int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets, int64_t segments,
+                                 int64_t cols, float *out, int32_t *tail_counts, void *stream) {
+    if (segments < 0 || segments > kMaxRows - 1 || cols < 0 || cols > kMaxSegmentCols || total_rows < 0 ||
+        total_rows > kMaxTotalRows)
+        return LOOM_ERR_RANGE;
+    if (segments == 0) return LOOM_OK;
+    if (!offsets || (!out && cols > 0) || (!x && total_rows > 0 && cols > 0)) return LOOM_ERR_NULL;
+    if (misaligned(offsets, 8) || misaligned(x, 4) || misaligned(out, 4) || misaligned(tail_counts, 4))
+        return LOOM_ERR_ALIGN;
+    loom_launch_config cfg;
+    const int64_t w[2] = {segments, cols};
+    if (int st = loom::evaluate_launch(loom::kSegmentSums, w, &cfg)) return st;
+    return launch_status(
+        loom::launch_segment_sums(cfg, x, total_rows, offsets, (int)cols, out, tail_counts, (hipStream_t)stream));
+}
+
+extern "C" int loom_i8_dequant_dot(const int32_t *w, const float *w_scale, const int32_t *x, const float *x_scale,
+                                   int64_t rows, int64_t k, int64_t batch, float *out, int32_t *acc, void *stream) {
+    if (k < 0 || k > loom::kMaxK || batch < 1 || batch > loom::kMaxBatch || rows < 0 || rows > kMaxRows)
+        return LOOM_ERR_RANGE;
+    if (k % 4 != 0) return LOOM_ERR_SHAPE;
+    if (rows == 0) return LOOM_OK;
+    if (!w_scale || !out || (k > 0 && (!w || !x))) return LOOM_ERR_NULL;
+    if (misaligned(w, 4) || misaligned(x, 4) || misaligned(w_scale, 4) || misaligned(x_scale, 4) ||
+        misaligned(out, 4) || misaligned(acc, 4))
+        return LOOM_ERR_ALIGN;
+    loom_launch_config cfg;
+    const int64_t wl[3] = {rows, k, batch};
+    if (int st = loom::evaluate_launch(loom::kI8DequantDot, wl, &cfg)) return st;
+    return launch_status(loom::launch_i8_dequant_dot(cfg, w, w_scale, x, x_scale, (int)rows, (int)(k / 4),
+                                                     (int)batch, out, acc, (hipStream_t)stream));
+}

@@ -1,0 +1,124 @@
+// device_common.hpp -- gfx950 (CDNA4, wave64) building blocks shared by the
+// streaming-reduction kernels: wave reductions and the read-ahead pipeline.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace loom {
+
+constexpr int kWave = 64;          // gfx950 wavefront width
+
+typedef int   int4v   __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// ---------------------------------------------------------------- cross-lane moves
+// DPP controls (GFX9 encoding): quad_perm[1,0,3,2], quad_perm[2,3,0,1],
+// row_half_mirror (lane i <- 7-i within 8), row_mirror (lane i <- 15-i within 16).
+constexpr int kDppQuadSwap1 = 0xB1;
+constexpr int kDppQuadSwap2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+// ds_swizzle bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10 -> lane ^ 16
+// inside each group of 32 lanes.
+constexpr int kSwizzleXor16 = (0x10 << 10) | 0x1F;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ int swz16(int v) { return __builtin_amdgcn_ds_swizzle(v, kSwizzleXor16); }
+__device__ __forceinline__ float swz16(float v) {
+    return __builtin_bit_cast(float, swz16(__builtin_bit_cast(int, v)));
+}
+
+// Sum over each group of 32 lanes; every lane of a group receives the same
+// bits (each step adds two equal-shaped partial sums, and a + b == b + a).
+// All 64 lanes must be active.
+template <typename T>
+__device__ __forceinline__ T half_wave_sum(T v) {
+    v = v + dpp<kDppQuadSwap1>(v);
+    v = v + dpp<kDppQuadSwap2>(v);
+    v = v + dpp<kDppHalfMirror>(v);
+    v = v + dpp<kDppMirror>(v);
+    v = v + swz16(v);
+    return v;
+}
+
+__device__ __forceinline__ float readlane(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ int readlane(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+// Full wave64 sum, returned as a wave-uniform value (the subgroup reduction
+// of TUNE §Derive full tiles; the result reaches every lane).  All lanes must
+// be active.  For int the result is exact; for float the order is a fixed
+// tree: pairs, quads, eights, sixteens, the two 16-lane halves of each 32,
+// then the two 32-lane halves.
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+    v = half_wave_sum(v);
+    return readlane(v, 0) + readlane(v, 32);
+}
+
+// ---------------------------------------------------------------- read-ahead
+// Software pipeline over n records in source order (TUNE §Choose the control:
+// pipeline(depth); CTRL §Pipeline reads ahead of ordered computation).
+//
+//   load()      issues the next record's loads and returns the (pending) value;
+//               called exactly n times, in order.
+//   consume(v)  folds the oldest record into the ordered recurrence; called
+//               exactly n times, in order.
+//
+// DEPTH-1 records stay in flight ahead of the consumer.  Loops of at least
+// 2*DEPTH-1 records take the pipelined path: an unconditional startup issues
+// DEPTH-1 loads, the steady body (unrolled by DEPTH) issues one load and
+// consumes the oldest record per step, and the drain consumes the rest.  The
+// ring rotates by renaming, never by copying -- a slot receives its next load
+// right after its old value was consumed -- and every path into the steady
+// loop has issued the same loads in the same order, so the compiler keeps
+// partial vmcnt waits (DEPTH-1 loads stay pending across each consume and
+// across the backedge).  Shorter loops run serially; an empty loop issues no
+// load.
+template <int DEPTH, typename T, typename N, typename Load, typename Consume>
+__device__ __forceinline__ void pipelined(N n, Load&& load, Consume&& consume) {
+    if (DEPTH <= 1 || n < 2 * DEPTH - 1) {
+        for (N i = 0; i < n; ++i) {
+            T v = load();
+            consume(v);
+        }
+        return;
+    }
+    if constexpr (DEPTH > 1) {
+        T ring[DEPTH];
+#pragma unroll
+        for (int j = 0; j < DEPTH - 1; ++j) ring[j] = load();
+        N i = 0;
+        for (; i + 2 * DEPTH - 1 <= n; i += DEPTH) {
+#pragma unroll
+            for (int j = 0; j < DEPTH; ++j) {
+                ring[(j + DEPTH - 1) % DEPTH] = load();
+                consume(ring[j]);
+            }
+        }
+        // DEPTH-1 <= n - i <= 2*DEPTH-2 records remain, DEPTH-1 of them loaded.
+        const int rest = (int)(n - i);
+#pragma unroll
+        for (int j = 0; j < 2 * DEPTH - 1; ++j) {
+            if (j < DEPTH - 1 || j < rest) {
+                if (j + DEPTH - 1 < rest) ring[(j + DEPTH - 1) % DEPTH] = load();
+                consume(ring[j % DEPTH]);
+            }
+        }
+    }
+}
+
+}  // namespace loom

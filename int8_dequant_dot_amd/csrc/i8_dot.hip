@@ -1,0 +1,247 @@
+// i8_dot.hip -- packed signed-byte dequantization with dot accumulation on gfx950.
+//
+// TUNE = "Tune loop unrolling and pipelining" (Loom pages),
+// §Apply the same controls to a packed dot product: each record carries
+// packed signed bytes that are unpacked by sign extension and accumulated in
+// order.  Here the scales are factored out of the sum, so the accumulation is
+// exact int32 and order-free, and the dequantization is one epilogue per
+// output: out = (f32(acc) * w_scale[r]) * x_scale[b].
+//
+// Packed layout: int32 word j of a row holds elements 4j..4j+3 in bytes 0..3.
+// Both kernels consume whole 16-byte groups (4 words = 16 int8) per lane and
+// never unpack explicitly: v_dot4_i32_i8 and the int8 MFMA sign-extend the
+// bytes themselves.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace loom {
+
+// 16-byte group of words [c, c+4) of a row with kw words; words at or beyond
+// kw read as zero (they contribute nothing to any dot product).  VEC16: the
+// host proved every row start 16-byte aligned, so one 128-bit load serves;
+// otherwise the group is read as four dwords.
+template <bool FULL, bool VEC16>
+__device__ __forceinline__ int4v load_words(const int32_t *__restrict__ row, int c, int kw) {
+    if (VEC16 && (FULL || c + 4 <= kw)) return *reinterpret_cast<const int4v *>(row + c);
+    int4v v = {0, 0, 0, 0};
+    if (FULL || c + 0 < kw) v.x = row[c + 0];
+    if (FULL || c + 1 < kw) v.y = row[c + 1];
+    if (FULL || c + 2 < kw) v.z = row[c + 2];
+    if (FULL || c + 3 < kw) v.w = row[c + 3];
+    return v;
+}
+
+__device__ __forceinline__ int dot16(int4v a, int4v b, int acc) {
+    acc = __builtin_amdgcn_sdot4(a.x, b.x, acc, false);
+    acc = __builtin_amdgcn_sdot4(a.y, b.y, acc, false);
+    acc = __builtin_amdgcn_sdot4(a.z, b.z, acc, false);
+    acc = __builtin_amdgcn_sdot4(a.w, b.w, acc, false);
+    return acc;
+}
+
+// ----------------------------------------------------------------------------
+// Single vector (batch == 1): one wave owns one 8-row tile.  A record is one
+// 1 KiB column block of the k dimension: the activation group each lane
+// needs (16 bytes) and the 8 rows' weight groups at the same columns, so the
+// activation fragment is loaded once per record and reused by all 8 rows.
+// Rows past the end of the matrix (the tail tile) re-read the last row and
+// their results are dropped, so the loads need no guards.  After the stream,
+// each row's int32 partials are summed across the wave (exact) and lane r of
+// the tile applies row r's epilogue.
+// ----------------------------------------------------------------------------
+struct GemvRecord {
+    int4v xv;
+    int4v wv[kGemvTileRows];
+};
+
+template <bool FULL, bool VEC16, int DEPTH>
+__global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
+                                                        const int32_t *__restrict__ x,
+                                                        const float *__restrict__ x_scale, int rows, int kw,
+                                                        float *__restrict__ out, int32_t *__restrict__ acc_out) {
+    constexpr int kBlockWords = kWave * 4;
+    const int lane = lane_id();
+    const int row0 = blockIdx.x * kGemvTileRows;
+    const int nrows = min(kGemvTileRows, rows - row0);
+    const int records = (kw + kBlockWords - 1) / kBlockWords;
+
+    const int32_t *wrow[kGemvTileRows];
+#pragma unroll
+    for (int r = 0; r < kGemvTileRows; ++r) wrow[r] = w + (int64_t)min(row0 + r, rows - 1) * kw;
+
+    int lblk = 0;
+    int acc[kGemvTileRows];
+#pragma unroll
+    for (int r = 0; r < kGemvTileRows; ++r) acc[r] = 0;
+
+    pipelined<DEPTH, GemvRecord>(
+        records,
+        [&]() {
+            const int c = lblk * kBlockWords + lane * 4;
+            GemvRecord q;
+            q.xv = load_words<FULL, VEC16>(x, c, kw);
+#pragma unroll
+            for (int r = 0; r < kGemvTileRows; ++r) q.wv[r] = load_words<FULL, VEC16>(wrow[r], c, kw);
+            ++lblk;
+            return q;
+        },
+        [&](const GemvRecord &q) {
+#pragma unroll
+            for (int r = 0; r < kGemvTileRows; ++r) acc[r] = dot16(q.wv[r], q.xv, acc[r]);
+        });
+
+    int mine = 0;
+#pragma unroll
+    for (int r = 0; r < kGemvTileRows; ++r) {
+        const int total = wave_sum(acc[r]);
+        if (lane == r) mine = total;
+    }
+    if (lane < nrows) {
+        const int row = row0 + lane;
+        float y = (float)mine;
+        y = y * w_scale[row];
+        if (x_scale) y = y * x_scale[0];
+        out[row] = y;
+        if (acc_out) acc_out[row] = mine;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Several vectors (batch >= 2): the shared activations make this a dense
+// int8 contraction, so it runs on the matrix cores.  One wave owns a 16-row
+// tile and all k; each k step is one v_mfma_i32_16x16x64_i8:
+//   A (16 x 64, weights):  lane l holds 16 bytes of row (l & 15) at byte
+//                          offset 16*(l >> 4) of the 64-byte step;
+//   B (64 x 16, vectors):  lane l holds the same 16 byte positions of vector
+//                          (l & 15) (zero for vectors >= batch);
+//   D (16 x 16, int32):    lane l holds rows 4*(l >> 4) + i, i < 4, of
+//                          column (l & 15).
+// A and B use the same byte-to-k assignment in every lane, so the product
+// sums exactly the matching k positions whatever order the hardware uses
+// inside a step.  A record is S steps (S KiB of weights per wave); NT tiles
+// of 16 vectors cover batch <= 16 * NT.  The accumulators are exact int32.
+// ----------------------------------------------------------------------------
+template <int S, int NT>
+struct MfmaRecord {
+    int4v a[S];
+    int4v b[NT][S];
+};
+
+template <bool FULL, bool VEC16, int DEPTH, int S, int NT>
+__global__ __launch_bounds__(kWave) void i8_mfma_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
+                                                        const int32_t *__restrict__ x,
+                                                        const float *__restrict__ x_scale, int rows, int kw, int batch,
+                                                        float *__restrict__ out, int32_t *__restrict__ acc_out) {
+    constexpr int kStepWords = 16;  // 64 int8 per step
+    const int lane = lane_id();
+    const int m = lane & 15;
+    const int g = lane >> 4;
+    const int row0 = blockIdx.x * kMfmaTileRows;
+    const int32_t *wrow = w + (int64_t)min(row0 + m, rows - 1) * kw;
+    const int32_t *xrow[NT];
+    bool xlive[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int n = t * 16 + m;
+        xlive[t] = n < batch;
+        xrow[t] = x + (int64_t)min(n, batch - 1) * kw;
+    }
+    const int steps = (kw + kStepWords - 1) / kStepWords;
+    const int records = (steps + S - 1) / S;
+
+    int4v acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = int4v{0, 0, 0, 0};
+
+    int lrec = 0;
+    pipelined<DEPTH, MfmaRecord<S, NT>>(
+        records,
+        [&]() {
+            MfmaRecord<S, NT> q;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int c = (lrec * S + s) * kStepWords + g * 4;
+                q.a[s] = load_words<FULL, VEC16>(wrow, c, kw);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int4v v = load_words<FULL, VEC16>(xrow[t], c, kw);
+                    q.b[t][s] = xlive[t] ? v : int4v{0, 0, 0, 0};
+                }
+            }
+            ++lrec;
+            return q;
+        },
+        [&](const MfmaRecord<S, NT> &q) {
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(q.a[s], q.b[t][s], acc[t], 0, 0, 0);
+        });
+
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int n = t * 16 + m;
+        if (n >= batch) continue;
+        const float xs = x_scale ? x_scale[n] : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 4 * g + i;
+            if (row < rows) {
+                const int a = acc[t][i];
+                float y = (float)a;
+                y = y * w_scale[row];
+                if (x_scale) y = y * xs;
+                out[(int64_t)row * batch + n] = y;
+                if (acc_out) acc_out[(int64_t)row * batch + n] = a;
+            }
+        }
+    }
+}
+
+constexpr int kGemvDepth = 3;   // two 8 KiB records in flight per wave
+constexpr int kMfmaDepth = 4;   // three 4 KiB records in flight per wave
+constexpr int kMfmaSteps = 4;
+
+template <bool FULL, bool VEC16>
+static void launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
+                        const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
+                        int32_t *acc) {
+    if (batch <= 16)
+        i8_mfma_kernel<FULL, VEC16, kMfmaDepth, kMfmaSteps, 1>
+            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+    else if (batch <= 32)
+        i8_mfma_kernel<FULL, VEC16, kMfmaDepth, kMfmaSteps, 2>
+            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+    else
+        i8_mfma_kernel<FULL, VEC16, kMfmaDepth, kMfmaSteps, 4>
+            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+}
+
+hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,
+                                 const int32_t *x, const float *x_scale, int rows, int k_words, int batch,
+                                 float *out, int32_t *acc, hipStream_t stream) {
+    const dim3 grid(cfg.workgroups[0]), block(cfg.workgroup_size[0]);
+    const bool vec16 = (k_words % 4 == 0) && (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+    if (batch == 1) {
+        const bool full = k_words % (kWave * 4) == 0;
+        if (full && vec16)
+            i8_gemv_kernel<true, true, kGemvDepth><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, k_words, out, acc);
+        else if (vec16)
+            i8_gemv_kernel<false, true, kGemvDepth><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, k_words, out, acc);
+        else
+            i8_gemv_kernel<false, false, kGemvDepth><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, k_words, out, acc);
+    } else {
+        const bool full = k_words % (16 * kMfmaSteps) == 0;
+        if (full && vec16)
+            launch_mfma<true, true>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc);
+        else if (vec16)
+            launch_mfma<false, true>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc);
+        else
+            launch_mfma<false, false>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace loom

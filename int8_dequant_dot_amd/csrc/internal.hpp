@@ -1,0 +1,52 @@
+// internal.hpp -- declarations shared by the C ABI, the launch-configuration
+// table and the kernel launchers.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "loom.h"
+
+namespace loom {
+
+enum ExportId : uint32_t {
+    kCopyF32 = 0,
+    kRowSumTiles,
+    kRowSums,
+    kSegmentSums,
+    kI8DequantDot,
+    kExportCount
+};
+
+// Launch geometry owned by each kernel (LAUNCH §A kernel owns two signatures).
+// `workload` holds the export's workload arguments; returns a loom_status.
+int evaluate_launch(ExportId id, const int64_t *workload, loom_launch_config *out);
+
+// Rows per full tile ("Tune loop unrolling and pipelining", §Derive full
+// tiles from a ragged loop).
+constexpr int kTileRows = 8;
+
+// Rows per wave tile of the int8 kernels: the v_dot4 GEMV takes the pages'
+// 8-row tile, the MFMA kernel one 16-row matrix-core tile.
+constexpr int kGemvTileRows = 8;
+constexpr int kMfmaTileRows = 16;
+constexpr int kMaxBatch = 64;
+constexpr int64_t kMaxK = 131068;
+
+// Kernel launchers.  Arguments are already validated; geometry comes from
+// evaluate_launch.  Each returns the HIP launch status.
+hipError_t launch_copy_f32(const loom_launch_config &cfg, const float *in, float *out, int64_t n,
+                           hipStream_t stream);
+hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *values, int count,
+                                const float *initial, float *sums, int32_t *final_row,
+                                int32_t *tail_count, hipStream_t stream);
+hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int rows, int cols,
+                           int64_t row_stride, float *out, hipStream_t stream);
+hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
+                               const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
+                               hipStream_t stream);
+hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,
+                                 const int32_t *x, const float *x_scale, int rows, int k_words,
+                                 int batch, float *out, int32_t *acc, hipStream_t stream);
+
+}  // namespace loom

@@ -1,0 +1,112 @@
+// launch_config.cpp -- the launch-configuration "program" of every exported
+// kernel ("Kernels and launch configuration": §A kernel owns two signatures,
+// §Workload is not workgroup count, §Evaluate the compiled launch contract).
+//
+// Each kernel owns the map from its logical workload to a physical grid.  The
+// table is evaluated by loom_launch_config_invoke for embeddings and by every
+// entry point before it launches, so the host never repeats the arithmetic.
+// Pure host code: nothing here touches the device.
+#include <string.h>
+
+#include "internal.hpp"
+
+namespace loom {
+
+namespace {
+
+constexpr uint32_t kSubgroupSize = 64;             // gfx950 wave64
+constexpr int64_t kMaxGridX = 0x7FFFFFFF;          // HIP grid.x limit, in workgroups
+
+int set(loom_launch_config *c, int64_t workgroups, uint32_t workgroup_size, uint32_t storage) {
+    if (workgroups < 0 || workgroups > kMaxGridX) return LOOM_ERR_RANGE;
+    c->workgroups[0] = (uint32_t)workgroups;
+    c->workgroups[1] = 1;
+    c->workgroups[2] = 1;
+    c->workgroup_size[0] = workgroup_size;
+    c->workgroup_size[1] = 1;
+    c->workgroup_size[2] = 1;
+    c->cluster_size[0] = c->cluster_size[1] = c->cluster_size[2] = 1;
+    c->subgroup_size = kSubgroupSize;
+    c->workgroup_storage_bytes = storage;
+    return LOOM_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// copy_f32(n): one element per work-item, 256 per workgroup; 1009 -> 4.
+int geo_copy(const int64_t *w, loom_launch_config *c) {
+    if (w[0] < 0) return LOOM_ERR_RANGE;
+    return set(c, ceil_div(w[0], 256), 256, 0);
+}
+
+// row_sum_tiles(count): one wave64 walks the whole tile.
+int geo_row_sum_tiles(const int64_t *w, loom_launch_config *c) {
+    if (w[0] < 0) return LOOM_ERR_RANGE;
+    return set(c, 1, kSubgroupSize, 0);
+}
+
+// row_sums(rows, cols): one wave per tile of 8 rows (the last one the tail).
+int geo_row_sums(const int64_t *w, loom_launch_config *c) {
+    if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
+    return set(c, ceil_div(w[0], kTileRows), kSubgroupSize, 0);
+}
+
+// segment_sums(segments, cols): one wave per segment.
+int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
+    if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
+    return set(c, w[0], kSubgroupSize, 0);
+}
+
+// i8_dequant_dot(rows, k, batch): one wave per 8-row tile for one vector
+// (v_dot4 GEMV), per 16-row matrix-core tile for several.
+int geo_i8(const int64_t *w, loom_launch_config *c) {
+    if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
+    const int64_t tile = w[2] == 1 ? kGemvTileRows : kMfmaTileRows;
+    return set(c, ceil_div(w[0], tile), kSubgroupSize, 0);
+}
+
+struct Export {
+    const char *name;
+    size_t arity;
+    int (*geometry)(const int64_t *, loom_launch_config *);
+};
+
+const Export kExports[kExportCount] = {
+    {"copy_f32", 1, geo_copy},
+    {"row_sum_tiles", 1, geo_row_sum_tiles},
+    {"row_sums", 2, geo_row_sums},
+    {"segment_sums", 2, geo_segment_sums},
+    {"i8_dequant_dot", 3, geo_i8},
+};
+
+}  // namespace
+
+int evaluate_launch(ExportId id, const int64_t *workload, loom_launch_config *out) {
+    return kExports[id].geometry(workload, out);
+}
+
+}  // namespace loom
+
+extern "C" int loom_launch_config_lookup(const char *export_name, uint32_t *token) {
+    if (!export_name || !token) return LOOM_ERR_NULL;
+    for (uint32_t i = 0; i < loom::kExportCount; ++i)
+        if (strcmp(export_name, loom::kExports[i].name) == 0) {
+            *token = i + 1;  // 0 is never a valid token
+            return LOOM_OK;
+        }
+    return LOOM_ERR_UNKNOWN_EXPORT;
+}
+
+extern "C" int loom_launch_config_invoke(uint32_t token, const uint64_t *workload_bits, size_t workload_count,
+                                         loom_launch_config *out) {
+    if (!out || (!workload_bits && workload_count)) return LOOM_ERR_NULL;
+    if (token == 0 || token > loom::kExportCount) return LOOM_ERR_TOKEN;
+    const loom::Export &e = loom::kExports[token - 1];
+    if (workload_count != e.arity) return LOOM_ERR_TOKEN;
+    int64_t w[4];
+    for (size_t i = 0; i < workload_count; ++i) memcpy(&w[i], &workload_bits[i], sizeof(int64_t));
+    loom_launch_config tmp;
+    const int st = e.geometry(w, &tmp);
+    if (st == LOOM_OK) *out = tmp;
+    return st;
+}

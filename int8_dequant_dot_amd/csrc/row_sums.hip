@@ -1,0 +1,151 @@
+// row_sums.hip -- the tiled 32-lane row sum and the streaming row sum on gfx950.
+//
+// TUNE = "Tune loop unrolling and pipelining" (Loom pages).
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace loom {
+
+// ----------------------------------------------------------------------------
+// TUNE §Derive full tiles from a ragged loop (@guide.sum_full_tiles).
+//
+// One wave64 owns the whole [rows][32] tile.  The pages' subgroup is 32 lanes
+// wide (one lane per column); a gfx950 wave holds two such rows at once, so a
+// record is a pair of rows: lanes 0-31 load row 2p, lanes 32-63 row 2p+1
+// (128 B each, one coalesced 256 B access).  Each half reduces its own row,
+// and the two row totals are added to the carried sum in row order.  Full
+// tiles have an even row count, so pairs never straddle the tail; rows at or
+// beyond final_row are never read.
+// ----------------------------------------------------------------------------
+template <int DEPTH>
+__global__ __launch_bounds__(kWave) void row_sum_tiles_kernel(const float *__restrict__ values, int count,
+                                                              const float *__restrict__ initial,
+                                                              float *__restrict__ sums,
+                                                              int32_t *__restrict__ final_row,
+                                                              int32_t *__restrict__ tail_count) {
+    const int lane = lane_id();
+    const int col = lane & 31;
+    // The tile walk advances by 8 while at least 8 rows remain: it stops at
+    // the largest multiple of 8 not above count, leaving count mod 8 rows.
+    const int full_rows = count & ~(kTileRows - 1);
+    const int tail = count & (kTileRows - 1);
+
+    float sum = initial ? initial[col] : 0.0f;
+    const float *p = values + lane;  // row (lane >> 5), column (lane & 31)
+    pipelined<DEPTH, float>(
+        full_rows / 2,
+        [&]() {
+            float v = *p;
+            p += 2 * 32;
+            return v;
+        },
+        [&](float v) {
+            v = half_wave_sum(v);           // each 32-lane half: its row's total
+            sum = sum + readlane(v, 0);     // row 2p
+            sum = sum + readlane(v, 32);    // row 2p+1
+        });
+    if (lane < 32) sums[lane] = sum;
+    if (lane == 0) {
+        *final_row = full_rows;
+        *tail_count = tail;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Streaming row sums.  One wave owns one tile of 8 rows (the last tile holds
+// the rows mod 8 tail, so it is the separate guarded tile of TUNE §Derive
+// full tiles).  The tile is walked as one stream of records -- a record is
+// 64 lanes x VEC contiguous floats of one row (1 KiB for VEC = 4) -- so the
+// read-ahead crosses row boundaries without draining.  Each lane folds its
+// floats into a private partial; at the end of a row the wave64 reduction
+// gives the row total (TUNE §Give each motif its own schedule: vector loads
+// pre-reduced in registers, then one ordered update per row).
+// ----------------------------------------------------------------------------
+template <int VEC> struct vec_of;
+template <> struct vec_of<1> { typedef float type; };
+template <> struct vec_of<4> { typedef float4v type; };
+
+template <int VEC>
+__device__ __forceinline__ float fold(typename vec_of<VEC>::type v) {
+    if constexpr (VEC == 1) return v;
+    else return (v.x + v.y) + (v.z + v.w);
+}
+
+template <int VEC, bool FULL, int DEPTH>
+__global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict__ x, int rows, int cols,
+                                                         int64_t row_stride, float *__restrict__ out) {
+    typedef typename vec_of<VEC>::type V;
+    constexpr int kBlock = kWave * VEC;  // columns per record
+    const int lane = lane_id();
+    const int row0 = blockIdx.x * kTileRows;
+    const int nrows = min(kTileRows, rows - row0);
+    const int records_per_row = (cols + kBlock - 1) / kBlock;
+
+    // Producer cursor (wave-uniform, kept in SGPRs): the current row and the
+    // first column of the next record.  A lane's load address is that base
+    // plus its own 32-bit column offset.
+    const float *rp = x + (int64_t)row0 * row_stride;
+    int lcol = 0;
+    const int lane_col = lane * VEC;
+    // consumer state
+    V acc = V(0.0f);
+    int crec = 0, crow = 0;
+    float mine = 0.0f;
+
+    pipelined<DEPTH, V>(
+        nrows * records_per_row,
+        [&]() {
+            const float *bp = rp + lcol;
+            V v = V(0.0f);
+            if (FULL || lcol + lane_col < cols) v = *reinterpret_cast<const V *>(bp + lane_col);
+            lcol += kBlock;
+            if (lcol >= cols) {
+                lcol = 0;
+                rp += row_stride;
+            }
+            return v;
+        },
+        [&](V v) {
+            acc += v;
+            if (++crec == records_per_row) {
+                const float total = wave_sum(fold<VEC>(acc));
+                if (lane == crow) mine = total;
+                acc = V(0.0f);
+                crec = 0;
+                ++crow;
+            }
+        });
+    if (lane < nrows) out[row0 + lane] = mine;
+}
+
+constexpr int kRowSumTilesDepth = 4;   // one full tile (4 row pairs) in flight
+constexpr int kRowSumsDepth = 8;       // 7 KiB per wave in flight
+
+hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *values, int count,
+                                const float *initial, float *sums, int32_t *final_row,
+                                int32_t *tail_count, hipStream_t stream) {
+    row_sum_tiles_kernel<kRowSumTilesDepth>
+        <<<dim3(cfg.workgroups[0]), dim3(cfg.workgroup_size[0]), 0, stream>>>(values, count, initial, sums,
+                                                                              final_row, tail_count);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int rows, int cols,
+                           int64_t row_stride, float *out, hipStream_t stream) {
+    const dim3 grid(cfg.workgroups[0]), block(cfg.workgroup_size[0]);
+    const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (row_stride % 4 == 0) && (cols % 4 == 0);
+    if (vec4) {
+        if (cols % (kWave * 4) == 0)
+            row_sums_kernel<4, true, kRowSumsDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);
+        else
+            row_sums_kernel<4, false, kRowSumsDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);
+    } else {
+        if (cols % kWave == 0)
+            row_sums_kernel<1, true, kRowSumsDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);
+        else
+            row_sums_kernel<1, false, kRowSumsDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace loom

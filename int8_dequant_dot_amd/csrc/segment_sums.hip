@@ -1,0 +1,91 @@
+// segment_sums.hip -- per-segment column sums on gfx950.
+//
+// TUNE = "Tune loop unrolling and pipelining" (Loom pages).
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace loom {
+
+template <int VEC> struct seg_vec;
+template <> struct seg_vec<1> { typedef float type; };
+template <> struct seg_vec<4> { typedef float4v type; };
+
+// ----------------------------------------------------------------------------
+// TUNE §Keep one checked source for experiments (@sum_rows): each lane sums
+// its own column over the rows, one load and one add per row, in row order.
+// Here one wave owns one segment; a lane owns VEC adjacent columns of a
+// 64*VEC-column block (256 columns = one 1 KiB coalesced record per row for
+// VEC = 4) and walks the segment's rows in order -- the full 8-row tiles and
+// then the tail, which are consecutive -- with the next rows read ahead.  No
+// cross-lane reduction is needed, and every column's sum is the same in-order
+// f32 recurrence a serial loop computes.  Segments with bad offsets are
+// reported in-band and read nothing.
+// ----------------------------------------------------------------------------
+template <int VEC, bool FULL, int DEPTH>
+__global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__restrict__ x, int64_t total_rows,
+                                                             const int64_t *__restrict__ offsets, int cols,
+                                                             float *__restrict__ out,
+                                                             int32_t *__restrict__ tail_counts) {
+    typedef typename seg_vec<VEC>::type V;
+    constexpr int kBlock = kWave * VEC;
+    const int lane = lane_id();
+    const int64_t s = blockIdx.x;
+    const int64_t begin = offsets[s];
+    const int64_t end = offsets[s + 1];
+    float *o = out + s * cols;
+
+    if (!(begin >= 0 && begin <= end && end <= total_rows)) {
+        for (int c = lane; c < cols; c += kWave) o[c] = __builtin_nanf("");
+        if (lane == 0 && tail_counts) tail_counts[s] = -1;
+        return;
+    }
+    const int64_t length = end - begin;
+    if (lane == 0 && tail_counts) tail_counts[s] = (int32_t)(length & (kTileRows - 1));
+
+    for (int cb = 0; cb < cols; cb += kBlock) {
+        const int c = cb + lane * VEC;
+        const bool active = FULL || c < cols;
+        // Row base of the next load (wave-uniform) plus the lane's column.
+        const float *rp = x + begin * cols + cb;
+        const int lane_col = lane * VEC;
+        V acc = V(0.0f);
+        pipelined<DEPTH, V>(
+            length,
+            [&]() {
+                V v = V(0.0f);
+                if (active) v = *reinterpret_cast<const V *>(rp + lane_col);
+                rp += cols;
+                return v;
+            },
+            [&](V v) { acc += v; });
+        if (active) *reinterpret_cast<V *>(o + c) = acc;
+    }
+}
+
+constexpr int kSegmentDepth = 8;  // 7 rows (7 KiB per wave at 256 columns) in flight
+
+hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
+                               const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
+                               hipStream_t stream) {
+    const dim3 grid(cfg.workgroups[0]), block(cfg.workgroup_size[0]);
+    const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0) &&
+                      (cols % 4 == 0);
+    if (vec4) {
+        if (cols % (kWave * 4) == 0)
+            segment_sums_kernel<4, true, kSegmentDepth>
+                <<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out, tail_counts);
+        else
+            segment_sums_kernel<4, false, kSegmentDepth>
+                <<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out, tail_counts);
+    } else {
+        if (cols % kWave == 0)
+            segment_sums_kernel<1, true, kSegmentDepth>
+                <<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out, tail_counts);
+        else
+            segment_sums_kernel<1, false, kSegmentDepth>
+                <<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out, tail_counts);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace loom

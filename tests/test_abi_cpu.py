@@ -1,0 +1,203 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+symbol, evaluates launch geometry, and rejects bad arguments on the host
+before any device call (no GPU needed: every call here returns before the
+HIP runtime is touched).
+
+Pages: "Kernels and launch configuration" (§Workload is not workgroup count,
+§Evaluate the compiled launch contract).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from tests.golden import load as golden
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loom.h")
+
+
+@pytest.fixture(scope="module")
+def loom():
+    import int8_dequant_dot_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def lib(loom):
+    return loom.library()
+
+
+FAKE = 0x10000  # a 64 KiB-aligned non-null address; never dereferenced by these tests
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(loom_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(loom):
+    out = subprocess.run(["nm", "-D", "--defined-only", loom.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    names = declared_symbols()
+    assert len(names) >= 9
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+
+
+def test_library_built_for_gfx950_only(loom, tmp_path):
+    # the device code objects live in the library's .hip_fatbin bundle
+    blob = tmp_path / "fatbin.bin"
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", loom.LIB_PATH, str(blob)],
+                   check=True)
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-z]+)", blob.read_bytes()))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_status_strings(loom):
+    for st in range(0, -8, -1):
+        assert loom.status_string(st) and loom.status_string(st) != "unknown status"
+    assert loom.status_string(-99) == "unknown status"
+    assert loom.version() >= 100
+
+
+# ------------------------------------------------------------------ launch configuration
+
+def test_launch_config_page_example(loom):
+    tok = loom.launch_config_lookup("copy_f32")
+    for n, wg, expected in golden.launch_fill():
+        cfg = loom.launch_config_invoke(tok, [n])
+        assert cfg["workgroups"] == (expected, 1, 1)
+        assert cfg["workgroup_size"] == (wg, 1, 1)
+        assert cfg["subgroup_size"] == 64 and cfg["cluster_size"] == (1, 1, 1)
+        assert cfg["workgroup_storage_bytes"] == 0
+
+
+def test_launch_config_matches_oracle_geometry(loom):
+    tok = loom.launch_config_lookup("copy_f32")
+    for n in list(range(0, 2050)) + [2 ** 31, 2 ** 33 + 5]:
+        assert loom.launch_config_invoke(tok, [n])["workgroups"][0] == oracle.fill_workgroups(n, 256)
+
+
+def test_launch_config_tiles(loom):
+    rs = loom.launch_config_lookup("row_sums")
+    for rows in (0, 1, 7, 8, 9, 65536, 65537):
+        assert loom.launch_config_invoke(rs, [rows, 4096])["workgroups"][0] == -(-rows // 8)
+    seg = loom.launch_config_lookup("segment_sums")
+    assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"][0] == 16384
+    i8 = loom.launch_config_lookup("i8_dequant_dot")
+    assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 2048
+    assert loom.launch_config_invoke(i8, [28672, 8192, 8])["workgroups"][0] == 1792
+    assert loom.launch_config_invoke(i8, [17, 64, 2])["workgroups"][0] == 2
+    t = loom.launch_config_lookup("row_sum_tiles")
+    assert loom.launch_config_invoke(t, [63])["workgroups"] == (1, 1, 1)
+    assert loom.launch_config_invoke(t, [63])["workgroup_size"] == (64, 1, 1)
+
+
+def test_launch_config_errors(loom, lib):
+    with pytest.raises(loom.LoomError) as e:
+        loom.launch_config_lookup("no_such_kernel")
+    assert e.value.status == loom.ERR_UNKNOWN_EXPORT
+    tok = loom.launch_config_lookup("row_sums")
+    with pytest.raises(loom.LoomError) as e:
+        loom.launch_config_invoke(tok, [8])  # wrong arity
+    assert e.value.status == loom.ERR_TOKEN
+    with pytest.raises(loom.LoomError) as e:
+        loom.launch_config_invoke(99, [8, 8])
+    assert e.value.status == loom.ERR_TOKEN
+    with pytest.raises(loom.LoomError) as e:
+        loom.launch_config_invoke(0, [8, 8])
+    assert e.value.status == loom.ERR_TOKEN
+    with pytest.raises(loom.LoomError) as e:
+        loom.launch_config_invoke(tok, [-1, 8])
+    assert e.value.status == loom.ERR_RANGE
+    with pytest.raises(loom.LoomError) as e:  # grid beyond 2^31-1 workgroups
+        loom.launch_config_invoke(loom.launch_config_lookup("copy_f32"), [2 ** 31 * 256])
+    assert e.value.status == loom.ERR_RANGE
+    assert lib.loom_launch_config_lookup(None, None) == loom.ERR_NULL
+    assert lib.loom_launch_config_invoke(tok, None, 2, None) == loom.ERR_NULL
+    assert sorted(loom.EXPORTS) == sorted(
+        n for n in loom.EXPORTS if loom.launch_config_lookup(n) > 0)
+
+
+# ------------------------------------------------------------------ host-side validation
+# Each call below fails a documented check and must return before touching the device.
+
+def test_copy_validation(loom, lib):
+    assert lib.loom_copy_f32(FAKE, FAKE, -1, None) == loom.ERR_RANGE
+    assert lib.loom_copy_f32(None, None, 0, None) == loom.OK  # nothing to do, nothing launched
+    assert lib.loom_copy_f32(None, FAKE, 5, None) == loom.ERR_NULL
+    assert lib.loom_copy_f32(FAKE + 2, FAKE, 5, None) == loom.ERR_ALIGN
+
+
+def test_row_sum_tiles_validation(loom, lib):
+    f = lib.loom_row_sum_tiles
+    assert f(FAKE, 63, 64, None, FAKE, FAKE, FAKE, None) == loom.ERR_RANGE  # count > rows_alloc
+    assert f(FAKE, 63, -1, None, FAKE, FAKE, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, -1, 0, None, FAKE, FAKE, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, (1 << 26) + 1, 0, None, FAKE, FAKE, FAKE, None) == loom.ERR_RANGE
+    assert f(None, 63, 8, None, FAKE, FAKE, FAKE, None) == loom.ERR_NULL
+    assert f(FAKE, 63, 8, None, None, FAKE, FAKE, None) == loom.ERR_NULL
+    assert f(FAKE, 63, 8, None, FAKE, None, FAKE, None) == loom.ERR_NULL
+    assert f(FAKE, 63, 8, None, FAKE, FAKE, None, None) == loom.ERR_NULL
+    assert f(FAKE + 1, 63, 8, None, FAKE, FAKE, FAKE, None) == loom.ERR_ALIGN
+    assert f(FAKE, 63, 8, FAKE + 2, FAKE, FAKE, FAKE, None) == loom.ERR_ALIGN
+
+
+def test_row_sums_validation(loom, lib):
+    f = lib.loom_row_sums
+    assert f(FAKE, -1, 4, 4, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, 4, -1, 4, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, 1 << 31, 4, 4, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, 4, 8, 7, FAKE, None) == loom.ERR_SHAPE  # stride < cols
+    assert f(FAKE, 1 << 30, 4, 1 << 40, FAKE, None) == loom.ERR_RANGE  # extent overflows
+    assert f(None, 0, 4, 4, None, None) == loom.OK
+    assert f(None, 4, 4, 4, FAKE, None) == loom.ERR_NULL
+    assert f(FAKE, 4, 4, 4, None, None) == loom.ERR_NULL
+    assert f(FAKE + 2, 4, 4, 4, FAKE, None) == loom.ERR_ALIGN
+    assert f(FAKE, 4, 4, 4, FAKE + 1, None) == loom.ERR_ALIGN
+
+
+def test_segment_sums_validation(loom, lib):
+    f = lib.loom_segment_sums
+    assert f(FAKE, 10, FAKE, -1, 4, FAKE, None, None) == loom.ERR_RANGE
+    assert f(FAKE, 10, FAKE, 2, -1, FAKE, None, None) == loom.ERR_RANGE
+    assert f(FAKE, 10, FAKE, 2, (1 << 20) + 1, FAKE, None, None) == loom.ERR_RANGE
+    assert f(FAKE, -1, FAKE, 2, 4, FAKE, None, None) == loom.ERR_RANGE
+    assert f(FAKE, (1 << 40) + 1, FAKE, 2, 4, FAKE, None, None) == loom.ERR_RANGE
+    assert f(None, 0, None, 0, 4, None, None, None) == loom.OK
+    assert f(FAKE, 10, None, 2, 4, FAKE, None, None) == loom.ERR_NULL
+    assert f(FAKE, 10, FAKE, 2, 4, None, None, None) == loom.ERR_NULL
+    assert f(None, 10, FAKE, 2, 4, FAKE, None, None) == loom.ERR_NULL
+    assert f(FAKE, 10, FAKE + 4, 2, 4, FAKE, None, None) == loom.ERR_ALIGN
+    assert f(FAKE, 10, FAKE, 2, 4, FAKE, FAKE + 2, None) == loom.ERR_ALIGN
+
+
+def test_i8_validation(loom, lib):
+    f = lib.loom_i8_dequant_dot
+    assert f(FAKE, FAKE, FAKE, None, 4, 6, 1, FAKE, None, None) == loom.ERR_SHAPE  # k % 4
+    assert f(FAKE, FAKE, FAKE, None, 4, 131072, 1, FAKE, None, None) == loom.ERR_RANGE  # |acc| could overflow
+    assert f(FAKE, FAKE, FAKE, None, 4, -4, 1, FAKE, None, None) == loom.ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, None, 4, 64, 0, FAKE, None, None) == loom.ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, None, 4, 64, 65, FAKE, None, None) == loom.ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, None, -1, 64, 1, FAKE, None, None) == loom.ERR_RANGE
+    assert f(None, None, None, None, 0, 64, 1, None, None, None) == loom.OK
+    assert f(None, FAKE, FAKE, None, 4, 64, 1, FAKE, None, None) == loom.ERR_NULL
+    assert f(FAKE, None, FAKE, None, 4, 64, 1, FAKE, None, None) == loom.ERR_NULL
+    assert f(FAKE, FAKE, None, None, 4, 64, 1, FAKE, None, None) == loom.ERR_NULL
+    assert f(FAKE, FAKE, FAKE, None, 4, 64, 1, None, None, None) == loom.ERR_NULL
+    assert f(FAKE + 2, FAKE, FAKE, None, 4, 64, 1, FAKE, None, None) == loom.ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE + 1, 4, 64, 8, FAKE, None, None) == loom.ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, None, 4, 64, 8, FAKE, FAKE + 3, None) == loom.ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors(loom):
+    import torch
+    with pytest.raises(TypeError):
+        loom.row_sums(torch.zeros(4, 4))
+    with pytest.raises(TypeError):
+        loom.i8_dequant_dot(torch.zeros(4, 4, dtype=torch.int32), torch.zeros(4), torch.zeros(4, dtype=torch.int32))

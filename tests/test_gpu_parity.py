@@ -1,0 +1,345 @@
+"""GPU parity: the gfx950 HIP path (through the C ABI) against the CPU oracle.
+
+Gates:
+  * tail counts, row indices and int32 dot accumulators: bit-exact;
+  * f32 sums: |gpu - oracle| <= 1e-5 * (sum|x| + |initial|) per output, and the
+    same bound against the oracle's binary64 shadow sum;
+  * dequantized outputs: |gpu - oracle| <= 2e-5 * |oracle| (the epilogue is the
+    same two f32 products, so in practice bit-exact);
+  * segment sums: bit-exact (each column is the same in-order f32 recurrence).
+
+Small cases span several tiles and ragged tails and are compared element by
+element; the full workload sizes are compared on outputs sampled at random
+(the oracle regenerates the sampled rows from the counter-based generator).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_SUM = 1e-5
+REL_DQ = 2e-5
+
+
+@pytest.fixture(scope="module")
+def loom(device):
+    import int8_dequant_dot_amd as m
+    return m
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def assert_sum_close(gpu, ref, ref64, absum, extra=0.0, what=""):
+    gpu = np.asarray(gpu, np.float64)
+    bound = REL_SUM * (np.asarray(absum, np.float64) + extra) + 1e-30
+    err = np.abs(gpu - np.asarray(ref, np.float64))
+    assert np.all(err <= bound), f"{what}: max err {err.max()} vs bound at argmax {bound.ravel()[err.argmax()]}"
+    if ref64 is not None:
+        err64 = np.abs(gpu - np.asarray(ref64))
+        assert np.all(err64 <= bound), f"{what}: max err vs f64 {err64.max()}"
+
+
+# ------------------------------------------------------------------ generator: same bits on GPU
+
+def test_generators_identical_on_gpu(device):
+    for fn, kw in [(synth.normal, {}), (synth.uniform_pm1, {}), (synth.int8_uniform, {}),
+                   (synth.uniform_range, {"lo": 1e-3, "hi": 1e-2}), (synth.randint, {"lo": 0, "hi": 4096})]:
+        a = fn(7, 3, 12345, 100003, device="cpu", **kw)
+        b = fn(7, 3, 12345, 100003, device=device, **kw).cpu()
+        assert torch.equal(a, b), fn.__name__
+
+
+# ------------------------------------------------------------------ copy (launch geometry + guard)
+
+@pytest.mark.parametrize("n", [1, 255, 256, 257, 1009, 4099, 65536 * 3 + 7])
+def test_copy_f32(loom, device, n):
+    x = synth.normal(synth.COPY.seed, synth.S_VALUES, 0, n)
+    out = torch.full((n + 64,), -1.0, device=device)
+    loom.copy_f32(x.to(device), out)
+    o = _np(out)
+    assert np.array_equal(o[:n].view(np.uint32), oracle.copy_f32(x.numpy()).view(np.uint32))
+    assert np.all(o[n:] == -1.0)  # the over-dispatched tail stored nothing
+
+
+def test_copy_page_geometry(loom, device):
+    tok = loom.launch_config_lookup("copy_f32")
+    assert loom.launch_config_invoke(tok, [1009])["workgroups"][0] == oracle.fill_workgroups(1009) == 4
+
+
+# ------------------------------------------------------------------ tiled 32-lane row sum
+
+def test_row_sum_tiles_iota_exhaustive(loom, device):
+    # all 64 counts of a 63x32 iota tile (rows_alloc = 63) -> exact
+    iota = (1 + 32 * np.arange(63)[:, None] + np.arange(32)[None, :]).astype(np.float32)
+    v = torch.from_numpy(iota).to(device)
+    for count in range(64):
+        sums, fr, tc = loom.row_sum_tiles(v, count)
+        osums, ofr, otc = oracle.row_sum_tiles(iota, count)
+        assert (int(_np(fr)[0]), int(_np(tc)[0])) == (ofr, otc), count
+        assert np.array_equal(_np(sums), osums), count
+
+
+def test_row_sum_tiles_random_poisoned(loom, device):
+    # N(0,1) tile with per-lane initial values; every row at or beyond final_row is NaN
+    values, count0 = synth.tile_inputs()
+    init = synth.normal(synth.TILE.seed, synth.S_INITIAL, 0, 32)
+    for count in sorted({count0, 0, 1, 7, 8, 9, 15, 16, 55, 56, 63}):
+        F = 8 * (count // 8)
+        v = values.numpy()[:count].copy()  # exact-size allocation: rows_alloc == count
+        v[F:] = np.nan
+        dv = torch.from_numpy(v).to(device)
+        sums, fr, tc = loom.row_sum_tiles(dv, count, init.to(device))
+        osums, ofr, otc = oracle.row_sum_tiles(values.numpy(), count, init.numpy())
+        assert (int(_np(fr)[0]), int(_np(tc)[0])) == (ofr, otc)
+        g = _np(sums)
+        assert np.all(np.isfinite(g)), count
+        absum = np.abs(values.numpy()[:F]).sum()
+        assert_sum_close(g, osums, None, absum, np.abs(init.numpy()), f"count {count}")
+
+
+def test_row_sum_tiles_long(loom, device):
+    # many tiles through the pipelined path, integer data (exact in any order)
+    rows = 1000
+    v = np.asarray(synth.randint(11, 0, 0, rows * 32, -8, 8).view(rows, 32), np.float32)
+    for count in (999, 1000, 64, 71):
+        sums, fr, tc = loom.row_sum_tiles(torch.from_numpy(v).to(device), count)
+        osums, ofr, otc = oracle.row_sum_tiles(v, count)
+        assert (int(_np(fr)[0]), int(_np(tc)[0])) == (ofr, otc)
+        assert np.array_equal(_np(sums), osums)
+
+
+# ------------------------------------------------------------------ streaming row sums
+
+ROW_SHAPES = [(1, 1), (7, 3), (8, 256), (9, 4096), (17, 4096), (23, 1000), (33, 260), (64, 4096), (13, 4097),
+              (5, 0), (3, 64), (41, 1024), (16, 8192)]
+
+
+@pytest.mark.parametrize("rows,cols", ROW_SHAPES)
+def test_row_sums_random(loom, device, rows, cols):
+    x = synth.dense_rows(synth.DENSE.seed, 0, rows, cols) if cols else torch.zeros(rows, 0)
+    g = _np(loom.row_sums(x.to(device)))
+    ref, d, a = oracle.row_sums(x.numpy())
+    assert_sum_close(g, ref, d, a, what=f"{rows}x{cols}")
+
+
+@pytest.mark.parametrize("rows,cols", [(19, 4096), (9, 37), (30, 256)])
+def test_row_sums_integer_exact(loom, device, rows, cols):
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    x = (((r * 7 + c * 3) % 9) - 4).astype(np.float32)
+    g = _np(loom.row_sums(torch.from_numpy(x).to(device)))
+    assert np.array_equal(g, oracle.row_sums(x)[0])
+
+
+@pytest.mark.parametrize("rows,cols,stride,offset", [(17, 4096, 4100, 0), (11, 300, 333, 0), (9, 256, 512, 1),
+                                                     (12, 1000, 1003, 3)])
+def test_row_sums_strided_poisoned(loom, device, rows, cols, stride, offset):
+    # padding between rows is NaN and must never be read; an odd base offset
+    # takes the 32-bit load path
+    full = synth.dense_rows(synth.DENSE.seed, 0, rows, stride + offset).numpy().copy()
+    full[:, :offset] = np.nan
+    full[:, offset + cols:] = np.nan
+    dx = torch.from_numpy(full).to(device)[:, offset:offset + cols]
+    g = _np(loom.row_sums(dx))
+    ref, d, a = oracle.row_sums(full[:, offset:offset + cols])
+    assert_sum_close(g, ref, d, a, what="strided")
+
+
+def test_row_sums_full_size_sampled(loom, device):
+    rows, cols = 65536, 4096
+    x = synth.dense_matrix(synth.DENSE.seed, rows, cols, device=device)
+    g = _np(loom.row_sums(x))
+    rng = np.random.default_rng(0)
+    sample = np.unique(np.concatenate([[0, 7, 8, rows - 1], rng.integers(0, rows, 60)]))
+    xs = torch.cat([synth.dense_rows(synth.DENSE.seed, int(r), 1, cols) for r in sample])
+    assert torch.equal(xs[-1].to(device), x[int(sample[-1])])  # GPU input == regenerated rows
+    ref, d, a = oracle.row_sums(xs.numpy())
+    assert_sum_close(g[sample], ref, d, a, what="65536x4096 sampled")
+    # every row: the sum of a U[-1,1) row of 4096 is far below 4096 in magnitude
+    assert np.all(np.isfinite(g)) and np.all(np.abs(g) < 1024)
+
+
+# ------------------------------------------------------------------ segment sums
+
+SEG_CASES = [
+    ([0, 1, 7, 8, 9, 15, 16, 17, 0, 100, 3], 256),
+    ([5, 0, 64, 13], 4),
+    ([9, 31, 2], 100),        # 128-bit path, partial column block
+    ([17, 8, 1], 257),        # 32-bit path (cols % 4 != 0)
+    ([40, 0, 23], 512),       # two column blocks
+    ([0, 0], 256),
+    ([1000, 3, 511], 256),    # long segments through the steady loop
+]
+
+
+@pytest.mark.parametrize("lengths,cols", SEG_CASES)
+def test_segment_sums_exact(loom, device, lengths, cols):
+    L = torch.tensor(lengths, dtype=torch.int64)
+    off = synth.segment_offsets(L)
+    x = synth.segment_rows(synth.SEGMENTS.seed, 0, int(off[-1]), cols)
+    out, tails = loom.segment_sums(x.to(device), off.to(device))
+    ref, rtails, _, _ = oracle.segment_sums(x.numpy(), off.numpy())
+    g = _np(out)
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))  # includes +0.0 for empty segments
+    assert np.array_equal(_np(tails), rtails)
+
+
+def test_segment_sums_page_vectors(loom, device):
+    # the pages' printed column sums of the 64x32 iota, as one segment each
+    from tests.golden import load as golden
+    iota = (1 + 32 * np.arange(64)[:, None] + np.arange(32)[None, :]).astype(np.float32)
+    cases = golden.sum_rows_iota()
+    # segment i covers the first n rows of its own copy of the iota
+    xs, offs = [], [0]
+    for _, n, _, _ in cases:
+        xs.append(iota[:n])
+        offs.append(offs[-1] + n)
+    xcat = np.concatenate(xs)
+    out, tails = loom.segment_sums(torch.from_numpy(xcat).to(device), torch.tensor(offs, device=device))
+    g = _np(out)
+    for i, (case, n, offset, step) in enumerate(cases):
+        assert np.array_equal(g[i], (offset + step * np.arange(32)).astype(np.float32)), case
+        assert int(_np(tails)[i]) == n % 8
+
+
+def test_segment_sums_bad_offsets_reported(loom, device):
+    x = torch.ones(10, 8, device=device)
+    off = torch.tensor([0, 4, 3, 12, 12], device=device)  # decreasing, then beyond total_rows
+    out, tails = loom.segment_sums(x, off)
+    g, t = _np(out), _np(tails)
+    assert np.all(g[0] == 4.0) and np.all(np.isnan(g[1])) and np.all(np.isnan(g[2]))
+    assert list(t) == [4, -1, -1, -1]
+    assert np.all(np.isnan(g[3]))  # [12, 12) lies beyond the 10 rows
+
+
+def test_segment_sums_full_size_sampled(loom, device):
+    S, cols = 16384, 256
+    L = synth.segment_lengths(synth.SEGMENTS.seed, S, 4096)
+    off = synth.segment_offsets(L)
+    total = int(off[-1])
+    x = synth.segment_matrix(synth.SEGMENTS.seed, total, cols, device=device)
+    out, tails = loom.segment_sums(x, off.to(device))
+    g, t = _np(out), _np(tails)
+    assert np.array_equal(t, (L.numpy() % 8).astype(np.int32))
+    rng = np.random.default_rng(1)
+    longest = int(L.argmax())
+    sample = np.unique(np.concatenate([[0, S - 1, longest], np.flatnonzero(L.numpy() == 0)[:2],
+                                       rng.integers(0, S, 24)]))
+    del x
+    torch.cuda.empty_cache()
+    for s in sample:
+        b, e = int(off[s]), int(off[s + 1])
+        xs = synth.segment_rows(synth.SEGMENTS.seed, b, e - b, cols)
+        ref, _, _, _ = oracle.segment_sums(xs.numpy(), np.array([0, e - b]))
+        assert np.array_equal(g[s].view(np.uint32), ref[0].view(np.uint32)), s
+
+
+# ------------------------------------------------------------------ int8 dequant dot
+
+def _i8_case(seed, rows, k, batch, with_xscale=True):
+    w = synth.i8_rows(seed, synth.S_W, 0, rows, k)
+    x = synth.i8_rows(seed, synth.S_X, 0, batch, k)
+    ws = synth.scales(seed, synth.S_WSCALE, 0, rows)
+    xs = synth.scales(seed, synth.S_XSCALE, 0, batch) if with_xscale else None
+    return w, x, ws, xs
+
+
+def _run_i8(loom, device, w, x, ws, xs):
+    y, acc = loom.i8_dequant_dot(loom.pack_int8(w.to(device)), ws.to(device), loom.pack_int8(x.to(device)),
+                                 None if xs is None else xs.to(device), want_acc=True)
+    return _np(y), _np(acc)
+
+
+def _check_i8(gy, gacc, w, x, ws, xs, what):
+    ry, racc = oracle.i8_dequant_dot(w.numpy(), ws.numpy(), x.numpy(), None if xs is None else xs.numpy())
+    assert np.array_equal(gacc, racc), f"{what}: acc mismatch"
+    err = np.abs(gy.astype(np.float64) - ry)
+    assert np.all(err <= REL_DQ * np.abs(ry)), f"{what}: max rel err {np.max(err / np.maximum(np.abs(ry), 1e-30))}"
+
+
+I8_CASES = [
+    # (rows, k, batch) -- batch 1 runs v_dot4, batch >= 2 the MFMA kernel
+    (1, 4, 1), (7, 4, 1), (8, 1024, 1), (9, 1028, 1), (17, 8192, 1), (33, 1040, 1), (100, 2112, 1), (5, 0, 1),
+    (3, 64, 2), (15, 256, 3), (16, 260, 8), (17, 1000, 8), (100, 8192, 8), (33, 64, 16), (40, 512, 17),
+    (20, 1024, 32), (18, 320, 33), (16, 4096, 64), (1, 4, 2), (31, 8, 5),
+]
+
+
+@pytest.mark.parametrize("rows,k,batch", I8_CASES)
+def test_i8_dequant_dot(loom, device, rows, k, batch):
+    w, x, ws, xs = _i8_case(100 + rows + k + batch, rows, k, batch, with_xscale=(batch % 2 == 0))
+    gy, gacc = _run_i8(loom, device, w, x, ws, xs)
+    _check_i8(gy, gacc, w, x, ws, xs, f"{rows}x{k}x{batch}")
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_i8_extremes_at_int32_limit(loom, device, batch):
+    # k = 131068 with every byte -128: acc = 16384 k = 2^31 - 65536, the largest
+    # accumulator the range check admits; the opposite sign on half the vectors
+    k, rows = 131068, 17
+    w = torch.full((rows, k), -128, dtype=torch.int8)
+    x = torch.full((batch, k), -128, dtype=torch.int8)
+    x[1::2] = 127
+    ws = torch.ones(rows)
+    xs = torch.ones(batch) if batch > 1 else None
+    gy, gacc = _run_i8(loom, device, w, x, ws, xs)
+    assert gacc[0, 0] == 16384 * k
+    if batch > 1:
+        assert gacc[0, 1] == -16256 * k
+    _check_i8(gy, gacc, w, x, ws, xs, "extremes")
+
+
+def test_i8_one_hot_and_byte_order(loom, device):
+    # one-hot activations pick single weight columns: pins byte order and
+    # sign extension through the packed words on both kernels
+    rows, k = 24, 256
+    w = synth.i8_rows(5, synth.S_W, 0, rows, k)
+    for batch in (1, 8):
+        cols = [3, 64, 129, 255, 0, 17, 18, 19][:batch]
+        x = torch.zeros(batch, k, dtype=torch.int8)
+        for b, c in enumerate(cols):
+            x[b, c] = 1
+        gy, gacc = _run_i8(loom, device, w, x, torch.ones(rows), None)
+        assert np.array_equal(gacc, w.numpy()[:, cols].astype(np.int32))
+
+
+def _i8_full(loom, device, wl, rows, k, batch):
+    seed = wl.seed
+    w = synth.i8_matrix(seed, synth.S_W, rows, k, device=device)
+    x = synth.i8_matrix(seed, synth.S_X, batch, k, device=device)
+    ws = synth.scales(seed, synth.S_WSCALE, 0, rows, device=device)
+    xs = synth.scales(seed, synth.S_XSCALE, 0, batch, device=device) if batch > 1 else None
+    y, acc = loom.i8_dequant_dot(loom.pack_int8(w), ws, loom.pack_int8(x), xs, want_acc=True)
+    gy, gacc = _np(y), _np(acc)
+    rng = np.random.default_rng(2)
+    sample = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 48)]))
+    wsamp = torch.cat([synth.i8_rows(seed, synth.S_W, int(r), 1, k) for r in sample])
+    assert torch.equal(wsamp[0].to(device), w[int(sample[0])])
+    xcpu = synth.i8_rows(seed, synth.S_X, 0, batch, k)
+    wscpu = synth.scales(seed, synth.S_WSCALE, 0, rows)[torch.from_numpy(sample)]
+    xscpu = synth.scales(seed, synth.S_XSCALE, 0, batch) if batch > 1 else None
+    _check_i8(gy[sample], gacc[sample], wsamp, xcpu, wscpu, xscpu, f"{rows}x{k}x{batch} sampled")
+
+
+def test_i8_gemv_full_size_sampled(loom, device):
+    _i8_full(loom, device, synth.GEMV, 16384, 8192, 1)
+
+
+def test_i8_batched_full_size_sampled(loom, device):
+    _i8_full(loom, device, synth.BATCHED, 28672, 8192, 8)
+
+
+def test_tile_workload(loom, device):
+    # the pages' own tile: one 63x32 N(0,1) tile, seeded count
+    values, count = synth.tile_inputs()
+    sums, fr, tc = loom.row_sum_tiles(values.to(device), count)
+    osums, ofr, otc = oracle.row_sum_tiles(values.numpy(), count)
+    assert (int(_np(fr)[0]), int(_np(tc)[0])) == (ofr, otc)
+    assert_sum_close(_np(sums), osums, None, np.abs(values.numpy()[:ofr]).sum(), what="tile")
