@@ -4,13 +4,14 @@ One step is one pass of the whole hot path over resident synthetic inputs:
   1. row_sums        65536 x 4096 f32                        (1,074,003,968 B)
   2. i8_dequant_dot  16384 x 8192 int8 weights, 1 vector      (134,356,992 B, v_dot4)
   3. i8_dequant_dot  28672 x 8192 int8 weights, 8 vectors     (235,978,784 B, MFMA)
-Bytes are algorithmic (each input read once, each output written once).  The
-1 GiB row-sum stream between consecutive int8 launches evicts their weights from
-the 256 MB last-level cache, so every launch reads HBM.
+Bytes are algorithmic (each input read once, each output written once).  Every
+input is a ring of copies rotated per step, so no launch finds its operands in
+the 256 MB last-level cache: every launch reads HBM.
 
 Prints one JSON line.  `value` is total algorithmic bytes per step / time per
-step.  `roofline` is for the dominant kernel (row_sums): its algorithmic bytes
-/ its mean duration from HIP events on the launch stream.  `cpu_baseline` is
+step, timed over K back-to-back steps (phase A).  `roofline` is for the
+dominant kernel (row_sums): its algorithmic bytes / its mean duration over K
+back-to-back launches between two HIP events on the launch stream (phase B).  `cpu_baseline` is
 the CPU oracle on the same workload (also used to check the outputs).
 
   python bench.py [--steps K] [--warmup W] [--segments] [--calibrate-copy MiB]
@@ -84,19 +85,23 @@ def main():
         return
 
     # ---------------------------------------------------------------- inputs (resident in HBM)
+    # Each input is a ring of identical copies at different addresses, rotated
+    # every step, so no launch finds its operands in the 256 MB last-level
+    # cache whatever the loads' cache policy: row sums 2 x 1 GiB, GEMV
+    # weights 4 x 128 MiB, batched weights 3 x 224 MiB.
     t0 = time.time()
     R2, C2 = 65536, 4096
-    x2 = synth.dense_matrix(synth.DENSE.seed, R2, C2, device=dev)
+    x2 = [synth.dense_matrix(synth.DENSE.seed, R2, C2, device=dev) for _ in range(2)]
     out2 = torch.empty(R2, device=dev)
 
     R4, K4 = 16384, 8192
-    w4 = synth.i8_matrix(synth.GEMV.seed, synth.S_W, R4, K4, device=dev)
+    w4 = [synth.i8_matrix(synth.GEMV.seed, synth.S_W, R4, K4, device=dev) for _ in range(4)]
     x4 = synth.i8_matrix(synth.GEMV.seed, synth.S_X, 1, K4, device=dev)
     s4 = synth.scales(synth.GEMV.seed, synth.S_WSCALE, 0, R4, device=dev)
     out4 = torch.empty(R4, 1, device=dev)
 
     R5, K5, B5 = 28672, 8192, 8
-    w5 = synth.i8_matrix(synth.BATCHED.seed, synth.S_W, R5, K5, device=dev)
+    w5 = [synth.i8_matrix(synth.BATCHED.seed, synth.S_W, R5, K5, device=dev) for _ in range(3)]
     x5 = synth.i8_matrix(synth.BATCHED.seed, synth.S_X, B5, K5, device=dev)
     s5 = synth.scales(synth.BATCHED.seed, synth.S_WSCALE, 0, R5, device=dev)
     sx5 = synth.scales(synth.BATCHED.seed, synth.S_XSCALE, 0, B5, device=dev)
@@ -104,43 +109,55 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs generated in {time.time() - t0:.1f}s")
 
-    w4p, x4p, w5p, x5p = loom.pack_int8(w4), loom.pack_int8(x4), loom.pack_int8(w5), loom.pack_int8(x5)
+    w4p, x4p = [loom.pack_int8(w) for w in w4], loom.pack_int8(x4)
+    w5p, x5p = [loom.pack_int8(w) for w in w5], loom.pack_int8(x5)
     bytes2 = R2 * C2 * 4 + R2 * 4
     bytes4 = R4 * K4 + K4 + R4 * 4 + R4 * 4
     bytes5 = R5 * K5 + B5 * K5 + R5 * 4 + B5 * 4 + R5 * B5 * 4
     step_bytes = bytes2 + bytes4 + bytes5
 
     kernels = [
-        ("row_sums", bytes2, lambda: loom.row_sums(x2, out2)),
-        ("i8_dequant_dot_gemv", bytes4, lambda: loom.i8_dequant_dot(w4p, s4, x4p, None, out=out4)),
-        ("i8_dequant_dot_batched", bytes5, lambda: loom.i8_dequant_dot(w5p, s5, x5p, sx5, out=out5)),
+        ("row_sums", bytes2, lambda i: loom.row_sums(x2[i % 2], out2)),
+        ("i8_dequant_dot_gemv", bytes4, lambda i: loom.i8_dequant_dot(w4p[i % 4], s4, x4p, None, out=out4)),
+        ("i8_dequant_dot_batched", bytes5, lambda i: loom.i8_dequant_dot(w5p[i % 3], s5, x5p, sx5, out=out5)),
     ]
 
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
+    def step(i):
         for _, _, fn in kernels:
-            fn()
+            fn(i)
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
+    # Phase A: whole steps back to back, bracketed by two events.
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in kernels]
-          for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for s in range(K):
-        for j, (_, _, fn) in enumerate(kernels):
-            ev[s][j][0].record(stream)
-            fn()
-            ev[s][j][1].record(stream)
+    for i in range(K):
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
-    per_kernel_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(K)]))
-                     for j in range(len(kernels))]
+    ms_per_step = start.elapsed_time(end) / K
     log(f"timed {K} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    # Phase B: each kernel alone, K launches back to back (its input ring
+    # still rotating) between two events on the launch stream: its mean
+    # duration, with the event overhead amortised over K launches.
+    per_kernel_ms = []
+    for _, _, fn in kernels:
+        fn(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(K):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_kernel_ms.append(e0.elapsed_time(e1) / K)
 
     parts = {}
     for (name, nbytes, _), ms in zip(kernels, per_kernel_ms):
@@ -192,8 +209,8 @@ def main():
     check = None
     if not args.no_cpu:
         import oracle
-        hx2, hw4, hx4, hs4 = x2.cpu().numpy(), w4.cpu().numpy(), x4.cpu().numpy(), s4.cpu().numpy()
-        hw5, hx5, hs5, hsx5 = w5.cpu().numpy(), x5.cpu().numpy(), s5.cpu().numpy(), sx5.cpu().numpy()
+        hx2, hw4, hx4, hs4 = x2[0].cpu().numpy(), w4[0].cpu().numpy(), x4.cpu().numpy(), s4.cpu().numpy()
+        hw5, hx5, hs5, hsx5 = w5[0].cpu().numpy(), x5.cpu().numpy(), s5.cpu().numpy(), sx5.cpu().numpy()
         passes, t_cpu = 0, 0.0
         while passes == 0 or t_cpu < 10.0:
             t = time.perf_counter()

@@ -36,9 +36,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -48,18 +48,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile and link; always rebuilds (the build check must compile)."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, out: str = OUT, defines=()) -> str:
+    """Compile and link; always rebuilds (the build check must compile).
+
+    ``defines`` (e.g. ``["LOOM_ROW_SUMS_DEPTH=12"]``) override the kernels'
+    schedule constants for a tuning build written to ``out``."""
+    build_dir = BUILD if out == OUT else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, sources()))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), sources()))
+    tmp = out + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -16,6 +16,15 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// Load of data that is streamed exactly once (rows, segment rows, weights):
+// a non-temporal load, so the lines are not kept in the caches at the expense
+// of data that is reused (the int8 activations).  On MI355X this raises the
+// sustained read rate of per-wave contiguous streams by ~12%.
+template <typename V>
+__device__ __forceinline__ V load_stream(const V *p) {
+    return __builtin_nontemporal_load(p);
+}
+
 // ---------------------------------------------------------------- cross-lane moves
 // DPP controls (GFX9 encoding): quad_perm[1,0,3,2], quad_perm[2,3,0,1],
 // row_half_mirror (lane i <- 7-i within 8), row_mirror (lane i <- 15-i within 16).

@@ -16,13 +16,38 @@
 
 namespace loom {
 
+// Schedules (records in flight, record size, load policy).  Each kernel
+// instantiation owns its schedule; the macros let a tuning build override it.
+#ifndef LOOM_GEMV_DEPTH
+#define LOOM_GEMV_DEPTH 4        // three 4 KiB records in flight per wave
+#endif
+#ifndef LOOM_MFMA_DEPTH
+#define LOOM_MFMA_DEPTH 4        // three records in flight per wave
+#endif
+#ifndef LOOM_MFMA_STREAM
+// Cached weight loads in the MFMA kernel: each A fragment reads half of a
+// 128 B line per row and the next step reads the other half; non-temporal
+// loads measured ~8% slower here.
+#define LOOM_MFMA_STREAM 0
+#endif
+#ifndef LOOM_MFMA_STEPS
+#define LOOM_MFMA_STEPS 4        // k steps (KiB of weights per wave) per record
+#endif
+constexpr int kGemvDepth = LOOM_GEMV_DEPTH;
+constexpr int kMfmaDepth = LOOM_MFMA_DEPTH;
+constexpr int kMfmaSteps = LOOM_MFMA_STEPS;
+
 // 16-byte group of words [c, c+4) of a row with kw words; words at or beyond
 // kw read as zero (they contribute nothing to any dot product).  VEC16: the
 // host proved every row start 16-byte aligned, so one 128-bit load serves;
-// otherwise the group is read as four dwords.
-template <bool FULL, bool VEC16>
+// otherwise the group is read as four dwords.  STREAM: the row is read once
+// (weights), so the load is non-temporal; activations are reused and cached.
+template <bool FULL, bool VEC16, bool STREAM>
 __device__ __forceinline__ int4v load_words(const int32_t *__restrict__ row, int c, int kw) {
-    if (VEC16 && (FULL || c + 4 <= kw)) return *reinterpret_cast<const int4v *>(row + c);
+    if (VEC16 && (FULL || c + 4 <= kw)) {
+        const int4v *p = reinterpret_cast<const int4v *>(row + c);
+        return STREAM ? load_stream(p) : *p;
+    }
     int4v v = {0, 0, 0, 0};
     if (FULL || c + 0 < kw) v.x = row[c + 0];
     if (FULL || c + 1 < kw) v.y = row[c + 1];
@@ -40,10 +65,10 @@ __device__ __forceinline__ int dot16(int4v a, int4v b, int acc) {
 }
 
 // ----------------------------------------------------------------------------
-// Single vector (batch == 1): one wave owns one 8-row tile.  A record is one
+// Single vector (batch == 1): one wave owns one tile of kGemvTileRows rows.  A record is one
 // 1 KiB column block of the k dimension: the activation group each lane
-// needs (16 bytes) and the 8 rows' weight groups at the same columns, so the
-// activation fragment is loaded once per record and reused by all 8 rows.
+// needs (16 bytes) and the tile rows' weight groups at the same columns, so
+// the activation fragment is loaded once per record and reused by every row.
 // Rows past the end of the matrix (the tail tile) re-read the last row and
 // their results are dropped, so the loads need no guards.  After the stream,
 // each row's int32 partials are summed across the wave (exact) and lane r of
@@ -55,21 +80,26 @@ struct GemvRecord {
 };
 
 template <bool FULL, bool VEC16, int DEPTH>
-__global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
+__global__ __launch_bounds__(kWave * kGemvKSplit) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
                                                         const int32_t *__restrict__ x,
                                                         const float *__restrict__ x_scale, int rows, int kw,
                                                         float *__restrict__ out, int32_t *__restrict__ acc_out) {
     constexpr int kBlockWords = kWave * 4;
     const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
     const int row0 = blockIdx.x * kGemvTileRows;
     const int nrows = min(kGemvTileRows, rows - row0);
-    const int records = (kw + kBlockWords - 1) / kBlockWords;
+    // this wave's contiguous share of the k records
+    const int all_records = (kw + kBlockWords - 1) / kBlockWords;
+    const int per_wave = (all_records + kGemvKSplit - 1) / kGemvKSplit;
+    const int first = min(all_records, wave * per_wave);
+    const int records = min(all_records, first + per_wave) - first;
 
     const int32_t *wrow[kGemvTileRows];
 #pragma unroll
     for (int r = 0; r < kGemvTileRows; ++r) wrow[r] = w + (int64_t)min(row0 + r, rows - 1) * kw;
 
-    int lblk = 0;
+    int lblk = first;
     int acc[kGemvTileRows];
 #pragma unroll
     for (int r = 0; r < kGemvTileRows; ++r) acc[r] = 0;
@@ -79,9 +109,9 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
         [&]() {
             const int c = lblk * kBlockWords + lane * 4;
             GemvRecord q;
-            q.xv = load_words<FULL, VEC16>(x, c, kw);
+            q.xv = load_words<FULL, VEC16, false>(x, c, kw);
 #pragma unroll
-            for (int r = 0; r < kGemvTileRows; ++r) q.wv[r] = load_words<FULL, VEC16>(wrow[r], c, kw);
+            for (int r = 0; r < kGemvTileRows; ++r) q.wv[r] = load_words<FULL, VEC16, true>(wrow[r], c, kw);
             ++lblk;
             return q;
         },
@@ -95,6 +125,16 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
     for (int r = 0; r < kGemvTileRows; ++r) {
         const int total = wave_sum(acc[r]);
         if (lane == r) mine = total;
+    }
+    if constexpr (kGemvKSplit > 1) {
+        __shared__ int partial[kGemvKSplit][kGemvTileRows];
+        if (lane < kGemvTileRows) partial[wave][lane] = mine;
+        __syncthreads();
+        if (wave != 0) return;
+        if (lane < kGemvTileRows) {
+            mine = partial[0][lane];
+            for (int v = 1; v < kGemvKSplit; ++v) mine += partial[v][lane];
+        }
     }
     if (lane < nrows) {
         const int row = row0 + lane;
@@ -128,7 +168,7 @@ struct MfmaRecord {
 };
 
 template <bool FULL, bool VEC16, int DEPTH, int S, int NT>
-__global__ __launch_bounds__(kWave) void i8_mfma_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
+__global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
                                                         const int32_t *__restrict__ x,
                                                         const float *__restrict__ x_scale, int rows, int kw, int batch,
                                                         float *__restrict__ out, int32_t *__restrict__ acc_out) {
@@ -147,13 +187,18 @@ __global__ __launch_bounds__(kWave) void i8_mfma_kernel(const int32_t *__restric
         xrow[t] = x + (int64_t)min(n, batch - 1) * kw;
     }
     const int steps = (kw + kStepWords - 1) / kStepWords;
-    const int records = (steps + S - 1) / S;
+    const int wave = threadIdx.x / kWave;
+    // this wave's contiguous share of the k records
+    const int all_records = (steps + S - 1) / S;
+    const int per_wave = (all_records + kMfmaKSplit - 1) / kMfmaKSplit;
+    const int first = min(all_records, wave * per_wave);
+    const int records = min(all_records, first + per_wave) - first;
 
     int4v acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = int4v{0, 0, 0, 0};
 
-    int lrec = 0;
+    int lrec = first;
     pipelined<DEPTH, MfmaRecord<S, NT>>(
         records,
         [&]() {
@@ -161,10 +206,10 @@ __global__ __launch_bounds__(kWave) void i8_mfma_kernel(const int32_t *__restric
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const int c = (lrec * S + s) * kStepWords + g * 4;
-                q.a[s] = load_words<FULL, VEC16>(wrow, c, kw);
+                q.a[s] = load_words<FULL, VEC16, LOOM_MFMA_STREAM != 0>(wrow, c, kw);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const int4v v = load_words<FULL, VEC16>(xrow[t], c, kw);
+                    const int4v v = load_words<FULL, VEC16, false>(xrow[t], c, kw);
                     q.b[t][s] = xlive[t] ? v : int4v{0, 0, 0, 0};
                 }
             }
@@ -178,6 +223,24 @@ __global__ __launch_bounds__(kWave) void i8_mfma_kernel(const int32_t *__restric
                 for (int t = 0; t < NT; ++t)
                     acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(q.a[s], q.b[t][s], acc[t], 0, 0, 0);
         });
+
+    if constexpr (kMfmaKSplit > 1) {
+        // waves 1.. publish their partial tiles; wave 0 adds them in wave order
+        __shared__ int partial[kMfmaKSplit > 1 ? kMfmaKSplit - 1 : 1][NT][4][kWave];
+        if (wave > 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) partial[wave - 1][t][i][lane] = acc[t][i];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        for (int v = 0; v < kMfmaKSplit - 1; ++v)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][i] += partial[v][t][i][lane];
+    }
 
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -199,9 +262,6 @@ __global__ __launch_bounds__(kWave) void i8_mfma_kernel(const int32_t *__restric
     }
 }
 
-constexpr int kGemvDepth = 3;   // two 8 KiB records in flight per wave
-constexpr int kMfmaDepth = 4;   // three 4 KiB records in flight per wave
-constexpr int kMfmaSteps = 4;
 
 template <bool FULL, bool VEC16>
 static void launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,

@@ -26,10 +26,26 @@ int evaluate_launch(ExportId id, const int64_t *workload, loom_launch_config *ou
 // tiles from a ragged loop).
 constexpr int kTileRows = 8;
 
-// Rows per wave tile of the int8 kernels: the v_dot4 GEMV takes the pages'
-// 8-row tile, the MFMA kernel one 16-row matrix-core tile.
-constexpr int kGemvTileRows = 8;
+// Row tiles of the int8 kernels: the v_dot4 GEMV takes 4 rows per wave (more,
+// shorter waves measured faster on MI355X than the pages' 8-row tile for this
+// short kernel), the MFMA kernel one 16-row matrix-core tile.  KSPLIT waves of one workgroup
+// share a tile and split its k range; their int32 partials are combined
+// through LDS in wave order (exact).  Tuning builds may override the macros.
+#ifndef LOOM_GEMV_TILE_ROWS
+#define LOOM_GEMV_TILE_ROWS 4
+#endif
+#ifndef LOOM_GEMV_KSPLIT
+#define LOOM_GEMV_KSPLIT 1
+#endif
+#ifndef LOOM_MFMA_KSPLIT
+#define LOOM_MFMA_KSPLIT 1
+#endif
+constexpr int kGemvTileRows = LOOM_GEMV_TILE_ROWS;
+constexpr int kGemvKSplit = LOOM_GEMV_KSPLIT;
 constexpr int kMfmaTileRows = 16;
+constexpr int kMfmaKSplit = LOOM_MFMA_KSPLIT;
+// 16-vector column tiles the MFMA kernel needs for a batch.
+constexpr int mfma_col_tiles(int64_t batch) { return batch <= 16 ? 1 : batch <= 32 ? 2 : 4; }
 constexpr int kMaxBatch = 64;
 constexpr int64_t kMaxK = 131068;
 

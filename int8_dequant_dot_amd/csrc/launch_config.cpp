@@ -57,12 +57,16 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
     return set(c, w[0], kSubgroupSize, 0);
 }
 
-// i8_dequant_dot(rows, k, batch): one wave per 8-row tile for one vector
-// (v_dot4 GEMV), per 16-row matrix-core tile for several.
+// i8_dequant_dot(rows, k, batch): one workgroup per row tile -- the v_dot4
+// GEMV's tile for one vector, a 16-row matrix-core tile for several -- with
+// KSPLIT waves splitting k; the LDS holds the waves' partial accumulators.
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
-    const int64_t tile = w[2] == 1 ? kGemvTileRows : kMfmaTileRows;
-    return set(c, ceil_div(w[0], tile), kSubgroupSize, 0);
+    if (w[2] == 1)
+        return set(c, ceil_div(w[0], kGemvTileRows), kSubgroupSize * kGemvKSplit,
+                   kGemvKSplit > 1 ? kGemvKSplit * kGemvTileRows * 4 : 0);
+    return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * kMfmaKSplit,
+               (kMfmaKSplit - 1) * mfma_col_tiles(w[2]) * 4 * kSubgroupSize * 4);
 }
 
 struct Export {

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict
         [&]() {
             const float *bp = rp + lcol;
             V v = V(0.0f);
-            if (FULL || lcol + lane_col < cols) v = *reinterpret_cast<const V *>(bp + lane_col);
+            if (FULL || lcol + lane_col < cols) v = load_stream(reinterpret_cast<const V *>(bp + lane_col));
             lcol += kBlock;
             if (lcol >= cols) {
                 lcol = 0;
@@ -118,8 +118,16 @@ __global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict
     if (lane < nrows) out[row0 + lane] = mine;
 }
 
-constexpr int kRowSumTilesDepth = 4;   // one full tile (4 row pairs) in flight
-constexpr int kRowSumsDepth = 8;       // 7 KiB per wave in flight
+// Read-ahead depths (records in the ring).  Each kernel instantiation owns its
+// schedule; the macros let a tuning build override the defaults.
+#ifndef LOOM_ROW_SUM_TILES_DEPTH
+#define LOOM_ROW_SUM_TILES_DEPTH 4   // one full tile (4 row pairs) in flight
+#endif
+#ifndef LOOM_ROW_SUMS_DEPTH
+#define LOOM_ROW_SUMS_DEPTH 8        // 7 KiB per wave in flight
+#endif
+constexpr int kRowSumTilesDepth = LOOM_ROW_SUM_TILES_DEPTH;
+constexpr int kRowSumsDepth = LOOM_ROW_SUMS_DEPTH;
 
 hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *values, int count,
                                 const float *initial, float *sums, int32_t *final_row,

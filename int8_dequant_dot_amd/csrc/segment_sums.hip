@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
             length,
             [&]() {
                 V v = V(0.0f);
-                if (active) v = *reinterpret_cast<const V *>(rp + lane_col);
+                if (active) v = load_stream(reinterpret_cast<const V *>(rp + lane_col));
                 rp += cols;
                 return v;
             },
@@ -62,7 +62,10 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
     }
 }
 
-constexpr int kSegmentDepth = 8;  // 7 rows (7 KiB per wave at 256 columns) in flight
+#ifndef LOOM_SEGMENT_SUMS_DEPTH
+#define LOOM_SEGMENT_SUMS_DEPTH 8  // 7 rows (7 KiB per wave at 256 columns) in flight
+#endif
+constexpr int kSegmentDepth = LOOM_SEGMENT_SUMS_DEPTH;
 
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
                                const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
