@@ -95,7 +95,10 @@ __device__ __forceinline__ T wave_sum(T v) {
 // right after its old value was consumed -- and every path into the steady
 // loop has issued the same loads in the same order, so the compiler keeps
 // partial vmcnt waits (DEPTH-1 loads stay pending across each consume and
-// across the backedge).  Shorter loops run serially; an empty loop issues no
+// across the backedge).  A scheduling fence (CTRL §Control instruction
+// order: it orders instructions without waiting for loads) after each step's
+// load keeps the compiler from sinking future loads below older consumer work
+// such as LDS staging.  Shorter loops run serially; an empty loop issues no
 // load.
 template <int DEPTH, typename T, typename N, typename Load, typename Consume>
 __device__ __forceinline__ void pipelined(N n, Load&& load, Consume&& consume) {
@@ -115,6 +118,7 @@ __device__ __forceinline__ void pipelined(N n, Load&& load, Consume&& consume) {
 #pragma unroll
             for (int j = 0; j < DEPTH; ++j) {
                 ring[(j + DEPTH - 1) % DEPTH] = load();
+                __builtin_amdgcn_sched_barrier(0);
                 consume(ring[j]);
             }
         }

@@ -22,13 +22,13 @@ namespace loom {
 #define LOOM_GEMV_DEPTH 4        // three 4 KiB records in flight per wave
 #endif
 #ifndef LOOM_MFMA_DEPTH
-#define LOOM_MFMA_DEPTH 4        // three records in flight per wave
+#define LOOM_MFMA_DEPTH 3        // two 4 KiB records in flight per wave
 #endif
 #ifndef LOOM_MFMA_STREAM
-// Cached weight loads in the MFMA kernel: each A fragment reads half of a
-// 128 B line per row and the next step reads the other half; non-temporal
-// loads measured ~8% slower here.
-#define LOOM_MFMA_STREAM 0
+// Non-temporal weight loads.  With LDS staging every load instruction reads
+// whole 128 B lines; without it (fragments straight from memory, half a line
+// per row) the default policy measured faster.
+#define LOOM_MFMA_STREAM 1
 #endif
 #ifndef LOOM_MFMA_STEPS
 #define LOOM_MFMA_STEPS 4        // k steps (KiB of weights per wave) per record
@@ -161,23 +161,38 @@ __global__ __launch_bounds__(kWave * kGemvKSplit) void i8_gemv_kernel(const int3
 // inside a step.  A record is S steps (S KiB of weights per wave); NT tiles
 // of 16 vectors cover batch <= 16 * NT.  The accumulators are exact int32.
 // ----------------------------------------------------------------------------
+// Vector columns at or beyond the batch hold a clamped (valid) row; they are
+// zeroed where consumed, so the producer never waits on its own loads.
+__device__ __forceinline__ int4v live_b(int4v b, bool live) { return live ? b : int4v{0, 0, 0, 0}; }
+
 template <int S, int NT>
 struct MfmaRecord {
     int4v a[S];
     int4v b[NT][S];
 };
 
-template <bool FULL, bool VEC16, int DEPTH, int S, int NT>
+template <bool FULL, bool VEC16, bool STAGE, int DEPTH, int S, int NT>
 __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
                                                         const int32_t *__restrict__ x,
                                                         const float *__restrict__ x_scale, int rows, int kw, int batch,
                                                         float *__restrict__ out, int32_t *__restrict__ acc_out) {
+    static_assert(!STAGE || S == 4, "LDS staging moves 16 rows x 256 B (4 k steps) per record");
     constexpr int kStepWords = 16;  // 64 int8 per step
     const int lane = lane_id();
     const int m = lane & 15;
     const int g = lane >> 4;
     const int row0 = blockIdx.x * kMfmaTileRows;
     const int32_t *wrow = w + (int64_t)min(row0 + m, rows - 1) * kw;
+    // Staged loads: instruction i of a record reads rows 4i..4i+3 of the tile,
+    // 256 contiguous bytes each (lane: row 4i + (lane >> 4), chunk lane & 15).
+    const int srow = lane >> 4, schunk = lane & 15;
+    const int32_t *wstage[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wstage[i] = w + (int64_t)min(row0 + 4 * i + srow, rows - 1) * kw;
+    // Per-wave staging tile: 16 rows x 16 chunks of 16 B; chunk c of row r at
+    // slot 16 r + (c ^ r), so both the row-wise writes and the fragment reads
+    // (16 rows, one chunk each) fall on distinct banks.
+    __shared__ int4v stage[STAGE ? kMfmaKSplit : 1][STAGE ? 16 * 16 : 1];
     const int32_t *xrow[NT];
     bool xlive[NT];
 #pragma unroll
@@ -203,25 +218,44 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
         records,
         [&]() {
             MfmaRecord<S, NT> q;
+            if constexpr (STAGE) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    q.a[i] = load_words<FULL, VEC16, LOOM_MFMA_STREAM != 0>(wstage[i], (lrec * 16 + schunk) * 4, kw);
+            }
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const int c = (lrec * S + s) * kStepWords + g * 4;
-                q.a[s] = load_words<FULL, VEC16, LOOM_MFMA_STREAM != 0>(wrow, c, kw);
+                if constexpr (!STAGE) q.a[s] = load_words<FULL, VEC16, LOOM_MFMA_STREAM != 0>(wrow, c, kw);
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int4v v = load_words<FULL, VEC16, false>(xrow[t], c, kw);
-                    q.b[t][s] = xlive[t] ? v : int4v{0, 0, 0, 0};
-                }
+                for (int t = 0; t < NT; ++t) q.b[t][s] = load_words<FULL, VEC16, false>(xrow[t], c, kw);
             }
             ++lrec;
             return q;
         },
         [&](const MfmaRecord<S, NT> &q) {
+            if constexpr (STAGE) {
+                int4v *tile = stage[wave];
 #pragma unroll
-            for (int s = 0; s < S; ++s)
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * i + srow;
+                    tile[16 * r + (schunk ^ r)] = q.a[i];
+                }
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(q.a[s], q.b[t][s], acc[t], 0, 0, 0);
+                for (int s = 0; s < S; ++s) {
+                    const int4v a = tile[16 * m + ((4 * s + g) ^ m)];
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, live_b(q.b[t][s], xlive[t]), acc[t], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(q.a[s], live_b(q.b[t][s], xlive[t]), acc[t],
+                                                                        0, 0, 0);
+            }
         });
 
     if constexpr (kMfmaKSplit > 1) {
@@ -267,14 +301,15 @@ template <bool FULL, bool VEC16>
 static void launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
                         const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
                         int32_t *acc) {
+    constexpr bool kStage = kMfmaStage;
     if (batch <= 16)
-        i8_mfma_kernel<FULL, VEC16, kMfmaDepth, kMfmaSteps, 1>
+        i8_mfma_kernel<FULL, VEC16, kStage, kMfmaDepth, kMfmaSteps, 1>
             <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
     else if (batch <= 32)
-        i8_mfma_kernel<FULL, VEC16, kMfmaDepth, kMfmaSteps, 2>
+        i8_mfma_kernel<FULL, VEC16, kStage, kMfmaDepth, kMfmaSteps, 2>
             <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
     else
-        i8_mfma_kernel<FULL, VEC16, kMfmaDepth, kMfmaSteps, 4>
+        i8_mfma_kernel<FULL, VEC16, kStage, kMfmaDepth, kMfmaSteps, 4>
             <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
 }
 

@@ -38,12 +38,17 @@ constexpr int kTileRows = 8;
 #define LOOM_GEMV_KSPLIT 1
 #endif
 #ifndef LOOM_MFMA_KSPLIT
-#define LOOM_MFMA_KSPLIT 1
+#define LOOM_MFMA_KSPLIT 4    // 4 waves per 16-row tile: 7168 waves for 28672 rows
+#endif
+#ifndef LOOM_MFMA_STAGE
+#define LOOM_MFMA_STAGE 1     // weights reach the MFMA through a per-wave LDS tile
 #endif
 constexpr int kGemvTileRows = LOOM_GEMV_TILE_ROWS;
 constexpr int kGemvKSplit = LOOM_GEMV_KSPLIT;
 constexpr int kMfmaTileRows = 16;
 constexpr int kMfmaKSplit = LOOM_MFMA_KSPLIT;
+constexpr bool kMfmaStage = LOOM_MFMA_STAGE != 0;
+constexpr uint32_t kMfmaStageBytes = 16 * 256;  // per wave: 16 rows x 256 B
 // 16-vector column tiles the MFMA kernel needs for a batch.
 constexpr int mfma_col_tiles(int64_t batch) { return batch <= 16 ? 1 : batch <= 32 ? 2 : 4; }
 constexpr int kMaxBatch = 64;

@@ -66,7 +66,8 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
         return set(c, ceil_div(w[0], kGemvTileRows), kSubgroupSize * kGemvKSplit,
                    kGemvKSplit > 1 ? kGemvKSplit * kGemvTileRows * 4 : 0);
     return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * kMfmaKSplit,
-               (kMfmaKSplit - 1) * mfma_col_tiles(w[2]) * 4 * kSubgroupSize * 4);
+               (kMfmaKSplit - 1) * mfma_col_tiles(w[2]) * 4 * kSubgroupSize * 4 +
+                   (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));
 }
 
 struct Export {

@@ -91,7 +91,13 @@ def test_launch_config_tiles(loom):
     assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"][0] == 16384
     i8 = loom.launch_config_lookup("i8_dequant_dot")
     assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 4096  # 4-row GEMV tiles
-    assert loom.launch_config_invoke(i8, [28672, 8192, 8])["workgroups"][0] == 1792
+    cfg = loom.launch_config_invoke(i8, [28672, 8192, 8])
+    assert cfg["workgroups"][0] == 1792
+    # 4 waves split k per 16-row tile; LDS: 3 waves' int32 partial tiles (1 KiB
+    # each) + 4 per-wave 16x256 B weight staging tiles
+    assert cfg["workgroup_size"] == (256, 1, 1)
+    assert cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096
+    assert loom.launch_config_invoke(i8, [28672, 8192, 64])["workgroup_storage_bytes"] == 3 * 4 * 1024 + 4 * 4096
     assert loom.launch_config_invoke(i8, [17, 64, 2])["workgroups"][0] == 2
     t = loom.launch_config_lookup("row_sum_tiles")
     assert loom.launch_config_invoke(t, [63])["workgroups"] == (1, 1, 1)
