@@ -35,9 +35,11 @@ _lib = None
 
 
 def lib():
+    """The oracle library; LOOM_ORACLE_LIB names a prebuilt copy instead (used by
+    the mutation test to run the pins against an oracle with a planted mistake)."""
     global _lib
     if _lib is None:
-        l = ctypes.CDLL(build())
+        l = ctypes.CDLL(os.environ.get("LOOM_ORACLE_LIB") or build())
         i64, p = ctypes.c_int64, ctypes.c_void_p
         l.oracle_tile_split.argtypes = [i64, i64, p, p]
         l.oracle_fill_workgroups.argtypes = [i64, i64]
