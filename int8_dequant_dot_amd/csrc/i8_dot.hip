@@ -65,14 +65,18 @@ __device__ __forceinline__ int dot16(int4v a, int4v b, int acc) {
 }
 
 // ----------------------------------------------------------------------------
-// Single vector (batch == 1): one wave owns one tile of kGemvTileRows rows.  A record is one
-// 1 KiB column block of the k dimension: the activation group each lane
-// needs (16 bytes) and the tile rows' weight groups at the same columns, so
-// the activation fragment is loaded once per record and reused by every row.
-// Rows past the end of the matrix (the tail tile) re-read the last row and
-// their results are dropped, so the loads need no guards.  After the stream,
-// each row's int32 partials are summed across the wave (exact) and lane r of
-// the tile applies row r's epilogue.
+// Single vector (batch == 1).  Rows are taken in tiles of kGemvTileRows; one
+// wave owns kGemvTilesPerWave consecutive tiles and streams them as one
+// sequence of records, so the read-ahead runs across tile boundaries and the
+// ring fills once per wave rather than once per tile.  A record is one 1 KiB
+// column block of k: the activation group each lane needs (16 bytes) and the
+// tile rows' weight groups at the same columns, so the activation fragment
+// is loaded once per record and reused by every row of the tile.  Rows past
+// the end of the matrix re-read the last row and their results are dropped,
+// so no load needs a row guard.  At the end of each tile the rows' int32
+// partials are summed across the wave (exact) into the lane that owns the
+// row in the wave's block; one coalesced epilogue then scales and stores
+// every row of the wave.
 // ----------------------------------------------------------------------------
 struct GemvRecord {
     int4v xv;
@@ -80,63 +84,62 @@ struct GemvRecord {
 };
 
 template <bool FULL, bool VEC16, int DEPTH>
-__global__ __launch_bounds__(kWave * kGemvKSplit) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
+__global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
                                                         const int32_t *__restrict__ x,
                                                         const float *__restrict__ x_scale, int rows, int kw,
                                                         float *__restrict__ out, int32_t *__restrict__ acc_out) {
     constexpr int kBlockWords = kWave * 4;
+    constexpr int TR = kGemvTileRows;
+    static_assert(TR * kGemvTilesPerWave <= kWave, "one lane per row of the wave's block");
     const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    const int row0 = blockIdx.x * kGemvTileRows;
-    const int nrows = min(kGemvTileRows, rows - row0);
-    // this wave's contiguous share of the k records
-    const int all_records = (kw + kBlockWords - 1) / kBlockWords;
-    const int per_wave = (all_records + kGemvKSplit - 1) / kGemvKSplit;
-    const int first = min(all_records, wave * per_wave);
-    const int records = min(all_records, first + per_wave) - first;
+    const int row0 = blockIdx.x * (TR * kGemvTilesPerWave);
+    const int wave_rows = min(TR * kGemvTilesPerWave, rows - row0);
+    const int tiles = (wave_rows + TR - 1) / TR;
+    const int records_per_tile = (kw + kBlockWords - 1) / kBlockWords;
 
-    const int32_t *wrow[kGemvTileRows];
+    // producer cursor: tile, column block, and the tile's row pointers
+    int lblk = 0, ltile = 0;
+    const int32_t *wrow[TR];
 #pragma unroll
-    for (int r = 0; r < kGemvTileRows; ++r) wrow[r] = w + (int64_t)min(row0 + r, rows - 1) * kw;
-
-    int lblk = first;
-    int acc[kGemvTileRows];
+    for (int r = 0; r < TR; ++r) wrow[r] = w + (int64_t)min(row0 + r, rows - 1) * kw;
+    // consumer state
+    int acc[TR];
 #pragma unroll
-    for (int r = 0; r < kGemvTileRows; ++r) acc[r] = 0;
+    for (int r = 0; r < TR; ++r) acc[r] = 0;
+    int cblk = 0, ctile = 0, mine = 0;
 
     pipelined<DEPTH, GemvRecord>(
-        records,
+        tiles * records_per_tile,
         [&]() {
             const int c = lblk * kBlockWords + lane * 4;
             GemvRecord q;
             q.xv = load_words<FULL, VEC16, false>(x, c, kw);
 #pragma unroll
-            for (int r = 0; r < kGemvTileRows; ++r) q.wv[r] = load_words<FULL, VEC16, true>(wrow[r], c, kw);
-            ++lblk;
+            for (int r = 0; r < TR; ++r) q.wv[r] = load_words<FULL, VEC16, true>(wrow[r], c, kw);
+            if (++lblk == records_per_tile) {
+                lblk = 0;
+                ++ltile;
+#pragma unroll
+                for (int r = 0; r < TR; ++r) wrow[r] = w + (int64_t)min(row0 + ltile * TR + r, rows - 1) * kw;
+            }
             return q;
         },
         [&](const GemvRecord &q) {
 #pragma unroll
-            for (int r = 0; r < kGemvTileRows; ++r) acc[r] = dot16(q.wv[r], q.xv, acc[r]);
+            for (int r = 0; r < TR; ++r) acc[r] = dot16(q.wv[r], q.xv, acc[r]);
+            if (++cblk == records_per_tile) {
+#pragma unroll
+                for (int r = 0; r < TR; ++r) {
+                    const int total = wave_sum(acc[r]);
+                    if (lane == ctile * TR + r) mine = total;
+                    acc[r] = 0;
+                }
+                cblk = 0;
+                ++ctile;
+            }
         });
 
-    int mine = 0;
-#pragma unroll
-    for (int r = 0; r < kGemvTileRows; ++r) {
-        const int total = wave_sum(acc[r]);
-        if (lane == r) mine = total;
-    }
-    if constexpr (kGemvKSplit > 1) {
-        __shared__ int partial[kGemvKSplit][kGemvTileRows];
-        if (lane < kGemvTileRows) partial[wave][lane] = mine;
-        __syncthreads();
-        if (wave != 0) return;
-        if (lane < kGemvTileRows) {
-            mine = partial[0][lane];
-            for (int v = 1; v < kGemvKSplit; ++v) mine += partial[v][lane];
-        }
-    }
-    if (lane < nrows) {
+    if (lane < wave_rows) {
         const int row = row0 + lane;
         float y = (float)mine;
         y = y * w_scale[row];

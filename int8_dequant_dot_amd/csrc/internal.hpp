@@ -26,16 +26,16 @@ int evaluate_launch(ExportId id, const int64_t *workload, loom_launch_config *ou
 // tiles from a ragged loop).
 constexpr int kTileRows = 8;
 
-// Row tiles of the int8 kernels: the v_dot4 GEMV takes 4 rows per wave (more,
-// shorter waves measured faster on MI355X than the pages' 8-row tile for this
-// short kernel), the MFMA kernel one 16-row matrix-core tile.  KSPLIT waves of one workgroup
-// share a tile and split its k range; their int32 partials are combined
-// through LDS in wave order (exact).  Tuning builds may override the macros.
+// Row tiles of the int8 kernels.  The v_dot4 GEMV takes tiles of 4 rows and
+// one wave streams TILES_PER_WAVE consecutive tiles; the MFMA kernel takes one
+// 16-row matrix-core tile per workgroup, whose KSPLIT waves split the k range
+// and combine their int32 partials through LDS in wave order (exact).
+// Tuning builds may override the macros.
 #ifndef LOOM_GEMV_TILE_ROWS
 #define LOOM_GEMV_TILE_ROWS 4
 #endif
-#ifndef LOOM_GEMV_KSPLIT
-#define LOOM_GEMV_KSPLIT 1
+#ifndef LOOM_GEMV_TILES_PER_WAVE
+#define LOOM_GEMV_TILES_PER_WAVE 1
 #endif
 #ifndef LOOM_MFMA_KSPLIT
 #define LOOM_MFMA_KSPLIT 4    // 4 waves per 16-row tile: 7168 waves for 28672 rows
@@ -44,7 +44,7 @@ constexpr int kTileRows = 8;
 #define LOOM_MFMA_STAGE 1     // weights reach the MFMA through a per-wave LDS tile
 #endif
 constexpr int kGemvTileRows = LOOM_GEMV_TILE_ROWS;
-constexpr int kGemvKSplit = LOOM_GEMV_KSPLIT;
+constexpr int kGemvTilesPerWave = LOOM_GEMV_TILES_PER_WAVE;
 constexpr int kMfmaTileRows = 16;
 constexpr int kMfmaKSplit = LOOM_MFMA_KSPLIT;
 constexpr bool kMfmaStage = LOOM_MFMA_STAGE != 0;

@@ -57,14 +57,14 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
     return set(c, w[0], kSubgroupSize, 0);
 }
 
-// i8_dequant_dot(rows, k, batch): one workgroup per row tile -- the v_dot4
-// GEMV's tile for one vector, a 16-row matrix-core tile for several -- with
-// KSPLIT waves splitting k; the LDS holds the waves' partial accumulators.
+// i8_dequant_dot(rows, k, batch): for one vector, one wave per block of
+// TILES_PER_WAVE GEMV tiles; for several, one workgroup per 16-row
+// matrix-core tile whose KSPLIT waves split k (the LDS holds their partial
+// accumulators and the weight staging tiles).
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
     if (w[2] == 1)
-        return set(c, ceil_div(w[0], kGemvTileRows), kSubgroupSize * kGemvKSplit,
-                   kGemvKSplit > 1 ? kGemvKSplit * kGemvTileRows * 4 : 0);
+        return set(c, ceil_div(w[0], int64_t(kGemvTileRows) * kGemvTilesPerWave), kSubgroupSize, 0);
     return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * kMfmaKSplit,
                (kMfmaKSplit - 1) * mfma_col_tiles(w[2]) * 4 * kSubgroupSize * 4 +
                    (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));
