@@ -50,6 +50,9 @@ def lib():
         l.oracle_segment_sums.argtypes = [p, p, i64, i64, p, p, p, p]
         l.oracle_i8_dequant_dot.argtypes = [p, p, p, p, i64, i64, i64, p, p]
         l.oracle_i8_dequant_dot.restype = ctypes.c_int
+        l.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        l.oracle_f16_to_f32.restype = ctypes.c_float
+        l.oracle_packed_dot.argtypes = [p, p, p, i64, p, i64, i64, p, p, p]
         _lib = l
     return _lib
 
@@ -134,3 +137,27 @@ def i8_dequant_dot(w, w_scale, x, x_scale=None):
     if st != 0:
         raise OverflowError("int8 dot accumulator does not fit in int32")
     return out, acc
+
+
+def f16_to_f32(bits: int) -> float:
+    return lib().oracle_f16_to_f32(bits)
+
+
+def packed_dot(fields, scales, rhs, count: int, initial=None, shadows: bool = True):
+    """fields int32 [records][outputs], scales uint16 (binary16 bits) [records][outputs],
+    rhs f32 [records][streams][4] -> (out f32 [outputs], out_f64, sum |terms|)."""
+    fields = _arr(fields, np.int32)
+    scales = _arr(scales, np.uint16)
+    rhs = _arr(rhs, np.float32)
+    records, outputs = fields.shape
+    assert scales.shape == fields.shape and 0 <= count <= records
+    assert rhs.ndim == 3 and rhs.shape[0] >= count and rhs.shape[2] == 4
+    streams = rhs.shape[1]
+    init = None if initial is None else _arr(initial, np.float32)
+    out = np.empty(outputs, np.float32)
+    d = np.empty(outputs, np.float64) if shadows else None
+    a = np.empty(outputs, np.float64) if shadows else None
+    # the oracle reads rhs rows [0, count) with the row pitch of this array
+    lib().oracle_packed_dot(_ptr(fields), _ptr(scales), _ptr(rhs), streams, _ptr(init), count, outputs,
+                            _ptr(out), _ptr(d), _ptr(a))
+    return out, d, a

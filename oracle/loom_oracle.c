@@ -28,6 +28,7 @@
 #include <stdint.h>
 #include <stddef.h>
 #include <math.h>
+#include <string.h>
 
 /* [TUNE] §Derive full tiles from a ragged loop: the repeated scf.while walks
  * full tiles while at least `tile` records remain and returns the first row
@@ -190,4 +191,63 @@ int oracle_i8_dequant_dot(const int8_t *w, const float *w_scale, const int8_t *x
         }
     }
     return status;
+}
+
+/* IEEE 754 binary16 -> binary32 (exact): sign, 5-bit exponent with bias 15,
+ * 10-bit fraction; exponent 0 encodes zero and subnormals (fraction * 2^-24),
+ * exponent 31 encodes infinities and NaNs (fraction kept in the top bits). */
+float oracle_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    uint32_t exponent = (h >> 10) & 0x1F;
+    uint32_t fraction = h & 0x3FF;
+    uint32_t bits;
+    if (exponent == 0x1F) {
+        bits = sign | 0x7F800000u | (fraction << 13);
+    } else if (exponent != 0) {
+        bits = sign | ((exponent - 15 + 127) << 23) | (fraction << 13);
+    } else {
+        float magnitude = (float)fraction * 0x1p-24f;   /* exact: fraction < 2^10 */
+        float value = sign ? -magnitude : magnitude;
+        return value;
+    }
+    float out;
+    memcpy(&out, &bits, sizeof out);
+    return out;
+}
+
+/* [TUNE] §Apply the same controls to a packed dot product
+ * (@streaming_packed_s8_dot_read_ahead).  For every output o, starting from
+ * initial[o] (0 if NULL), each record r < count in order contributes
+ *     v_j = f32(sign-extended byte j of fields[r][o]) * f32(scales[r][o]),  j = 0..3
+ *     sum = sum + v_j * rhs[r][o mod streams][j]   for j = 0, 1, 2, 3 in order
+ * (the dot accumulates into the carried sum one product at a time; every
+ * product and sum is a separate f32 rounding).  fields and scales are
+ * record-major: [records][outputs]; scales are binary16 bit patterns; rhs is
+ * [records][streams][4] f32, the activation streams shared by the outputs. */
+void oracle_packed_dot(const int32_t *fields, const uint16_t *scales, const float *rhs, int64_t streams,
+                       const float *initial, int64_t count, int64_t outputs, float *out,
+                       double *out_f64, double *out_abs)
+{
+    for (int64_t o = 0; o < outputs; ++o) {
+        float sum = initial ? initial[o] : 0.0f;
+        double d = sum, a = fabs((double)sum);
+        int64_t stream = o % streams;
+        for (int64_t r = 0; r < count; ++r) {
+            uint32_t word = (uint32_t)fields[r * outputs + o];
+            float scale = oracle_f16_to_f32(scales[r * outputs + o]);
+            const float *act = rhs + (r * streams + stream) * 4;
+            for (int j = 0; j < 4; ++j) {
+                int8_t byte = (int8_t)(uint8_t)(word >> (8 * j));
+                float v = (float)byte * scale;
+                float p = v * act[j];
+                sum = sum + p;
+                d = d + (double)byte * (double)scale * (double)act[j];
+                a = a + fabs((double)byte * (double)scale * (double)act[j]);
+            }
+        }
+        out[o] = sum;
+        if (out_f64) out_f64[o] = d;
+        if (out_abs) out_abs[o] = a;
+    }
 }

@@ -31,6 +31,12 @@ MUTATIONS = {
                            "(int64_t)w[i * rows + r] * (int64_t)x[b * k + i]"),
     "vector scale index fixed": ("if (x_scale) y = y * x_scale[b];", "if (x_scale) y = y * x_scale[0];"),
     "row stride ignored": ("row_sum_one(x + r * row_stride, cols", "row_sum_one(x + r * cols, cols"),
+    "packed-dot bytes unsigned": ("int8_t byte = (int8_t)(uint8_t)(word >> (8 * j));",
+                                  "int byte = (uint8_t)(word >> (8 * j));"),
+    "packed-dot stream by division": ("int64_t stream = o % streams;", "int64_t stream = (o / streams) % streams;"),
+    "packed-dot scale ignored": ("float v = (float)byte * scale;", "float v = (float)byte;"),
+    "packed-dot byte order reversed": ("int8_t byte = (int8_t)(uint8_t)(word >> (8 * j));",
+                                       "int8_t byte = (int8_t)(uint8_t)(word >> (8 * (3 - j)));"),
 }
 
 

@@ -357,3 +357,89 @@ def test_generator_distributions():
     assert s.min() >= 1e-3 and s.max() <= 1e-2
     L = synth.segment_lengths(1, 20000, 4096).numpy()
     assert L.min() == 0 and L.max() == 4096
+
+
+# ------------------------------------------------------------------ packed dot (pages' literal form)
+# TUNE §Apply the same controls to a packed dot product
+
+def test_f16_decoder_all_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float32).view(np.uint32)
+    got = np.array([oracle.f16_to_f32(int(b)) for b in bits], np.float32).view(np.uint32)
+    nan = np.isnan(bits.view(np.float16))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(got[nan].view(np.float32)))
+
+
+def _packed(records, outputs, streams, seed=0):
+    rng = np.random.default_rng(seed)
+    fields = rng.integers(-2 ** 31, 2 ** 31, size=(records, outputs), dtype=np.int64).astype(np.int32)
+    scales = rng.uniform(1e-3, 1e-2, size=(records, outputs)).astype(np.float16).view(np.uint16)
+    rhs = rng.standard_normal((records, streams, 4)).astype(np.float32)
+    return fields, scales, rhs
+
+
+def test_packed_dot_empty_is_initial():
+    fields, scales, rhs = _packed(4, 70, 64)
+    init = np.linspace(-3, 3, 70).astype(np.float32)
+    assert np.array_equal(oracle.packed_dot(fields, scales, rhs, 0, init)[0], init)
+    assert np.array_equal(oracle.packed_dot(fields, scales, rhs, 0)[0], np.zeros(70, np.float32))
+
+
+def test_packed_dot_one_hot_selects_signed_bytes():
+    # unit scales and a one-hot activation pick byte j of every record: an exact
+    # integer sum that pins sign extension and the byte order of the word
+    records, outputs, streams = 9, 130, 64
+    fields, _, _ = _packed(records, outputs, streams, 1)
+    ones = np.full((records, outputs), 0x3C00, np.uint16)  # binary16 1.0
+    b = fields.view(np.uint8).reshape(records, outputs, 4).view(np.int8).astype(np.int64)
+    for j in range(4):
+        rhs = np.zeros((records, streams, 4), np.float32)
+        rhs[:, :, j] = 1.0
+        out = oracle.packed_dot(fields, ones, rhs, records)[0]
+        assert np.array_equal(out, b[:, :, j].sum(0).astype(np.float32)), j
+
+
+def test_packed_dot_stream_mapping_and_scale():
+    # every byte 1 in position 0, scale 2^-3, stream s carries activation s+1:
+    # output o accumulates count * 2^-3 * (o mod 64 + 1)
+    records, outputs, streams, count = 5, 200, 64, 4
+    fields = np.full((records, outputs), 1, np.int32)
+    scales = np.full((records, outputs), 0x3000, np.uint16)  # binary16 0.125
+    rhs = np.zeros((records, streams, 4), np.float32)
+    rhs[:, :, 0] = (np.arange(streams) + 1)[None, :]
+    out = oracle.packed_dot(fields, scales, rhs, count)[0]
+    assert np.array_equal(out, (count * 0.125 * (np.arange(outputs) % 64 + 1)).astype(np.float32))
+
+
+def test_packed_dot_serial_accumulation_order():
+    # the reading: each product is added to the carried sum in turn.  Starting
+    # at 2^24 with four products of 1.0, a serial f32 recurrence stays at 2^24
+    # (each +1 rounds away), while summing the products first would give 2^24+4.
+    fields = np.array([[0x01010101]], np.int32)
+    scales = np.array([[0x3C00]], np.uint16)
+    rhs = np.ones((1, 1, 4), np.float32)
+    out = oracle.packed_dot(fields, scales, rhs, 1, np.array([2.0 ** 24], np.float32))[0]
+    assert out[0] == np.float32(2.0 ** 24)
+
+
+def test_packed_dot_random_within_bound():
+    records, outputs, streams = 14, 40, 64
+    fields, scales, rhs = _packed(records, outputs, streams, 2)
+    init = np.random.default_rng(3).standard_normal(outputs).astype(np.float32)
+    out, d, a = oracle.packed_dot(fields, scales, rhs, records, init)
+    b = fields.view(np.uint8).reshape(records, outputs, 4).view(np.int8)
+    sc = scales.view(np.float16).astype(np.float64)
+    n = 4 * records
+    for o in range(outputs):
+        exact = Fraction(float(init[o]))
+        absum = abs(float(init[o]))
+        for r in range(records):
+            for j in range(4):
+                t = Fraction(int(b[r, o, j])) * Fraction(float(sc[r, o])) * Fraction(float(rhs[r, o % 64, j]))
+                exact += t
+                absum += abs(float(t))
+        # byte * scale is exact in f32 (8 x 11 significant bits); each product
+        # with the activation rounds once, then n recursive additions
+        assert abs(Fraction(float(out[o])) - exact) <= gamma(n + 1) * absum
+        assert abs(d[o] - float(exact)) <= gamma(n + 1, U64) * absum + 1e-300
