@@ -190,6 +190,25 @@ def main():
         del x3
         torch.cuda.empty_cache()
 
+    # The pages' literal packed-dot recurrence: at the pages' own shape (2048
+    # outputs x 128 records, latency-bound: microseconds per call) and at a
+    # large shape (262144 outputs x 128 records) for bandwidth.
+    for label, outputs in (("packed_dot_2048x128", 2048), ("packed_dot_262144x128", 262144)):
+        pf, ps, pr, pi = synth.packed_dot_inputs(records=128, outputs=outputs, device=dev)
+        pout = torch.empty(outputs, device=dev)
+        nbytes = 128 * outputs * 6 + pr.numel() * 4 + 2 * outputs * 4
+        loom.packed_dot(pf, ps, pr, 128, pi, out=pout)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(K):
+            loom.packed_dot(pf, ps, pr, 128, pi, out=pout)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        parts[label] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- roofline of the dominant kernel

@@ -78,6 +78,7 @@ typedef struct loom_launch_config {
  *   "row_sums"        (rows, cols)
  *   "segment_sums"    (segments, cols)
  *   "i8_dequant_dot"  (rows, k, batch)
+ *   "packed_dot"      (outputs, count, streams)
  * lookup: LOOM_ERR_NULL if a pointer is NULL, LOOM_ERR_UNKNOWN_EXPORT if no
  * kernel has that name.  The token stays valid for the life of the process. */
 int loom_launch_config_lookup(const char *export_name, uint32_t *token);
@@ -182,6 +183,33 @@ int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets
 int loom_i8_dequant_dot(const int32_t *w, const float *w_scale, const int32_t *x,
                         const float *x_scale, int64_t rows, int64_t k, int64_t batch,
                         float *out, int32_t *acc, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * The pages' literal packed signed-byte dot recurrence (TUNE §Apply the     *
+ * same controls to a packed dot product).  For every output o, starting     *
+ * from initial[o] (0 if NULL), every record r < count, in record order:     *
+ *     v_j = f32(signed byte j of fields[r][o]) * f32(scales[r][o])          *
+ *     sum = sum + v_j * rhs[r][o mod streams][j]     for j = 0, 1, 2, 3     *
+ * each product and sum a separate f32 rounding (no fused multiply-add), so  *
+ * the result is the serial recurrence bit for bit.                          *
+ *   fields  : int32[records][outputs], record-major (consecutive outputs    *
+ *             contiguous), 4-byte aligned (16-byte when outputs >= 65536,   *
+ *             outputs % 4 == 0 and streams % 4 == 0: then each lane takes   *
+ *             four outputs with 128-bit loads)                              *
+ *   scales  : binary16 bit patterns [records][outputs], 2-byte aligned      *
+ *             (8-byte in the four-outputs case)                             *
+ *   rhs     : f32[records][streams][4] activations, 16-byte aligned; the    *
+ *             streams are shared by all outputs (output o reads o mod       *
+ *             streams)                                                      *
+ *   streams : 1 <= streams < 2^31                                           *
+ *   initial : f32[outputs] or NULL                                          *
+ *   records : records allocated; 0 <= count <= records (LOOM_ERR_RANGE)     *
+ *   outputs : 0 <= outputs <= 2^31 * 255                                    *
+ *   out     : f32[outputs]                                                  *
+ * ------------------------------------------------------------------------ */
+int loom_packed_dot(const int32_t *fields, const uint16_t *scales, const float *rhs, int64_t streams,
+                    const float *initial, int64_t records, int64_t count, int64_t outputs, float *out,
+                    void *stream);
 
 #ifdef __cplusplus
 }

@@ -37,14 +37,15 @@ _lib.loom_row_sum_tiles.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _p]
 _lib.loom_row_sums.argtypes = [_p, _i64, _i64, _i64, _p, _p]
 _lib.loom_segment_sums.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p, _p]
 _lib.loom_i8_dequant_dot.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p]
+_lib.loom_packed_dot.argtypes = [_p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _p]
 for _name in ("loom_launch_config_lookup", "loom_launch_config_invoke", "loom_copy_f32", "loom_row_sum_tiles",
-              "loom_row_sums", "loom_segment_sums", "loom_i8_dequant_dot"):
+              "loom_row_sums", "loom_segment_sums", "loom_i8_dequant_dot", "loom_packed_dot"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 # status codes (include/loom.h)
 OK, ERR_NULL, ERR_RANGE, ERR_ALIGN, ERR_SHAPE, ERR_UNKNOWN_EXPORT, ERR_TOKEN, ERR_DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 
-EXPORTS = ("copy_f32", "row_sum_tiles", "row_sums", "segment_sums", "i8_dequant_dot")
+EXPORTS = ("copy_f32", "row_sum_tiles", "row_sums", "segment_sums", "i8_dequant_dot", "packed_dot")
 
 
 class LoomError(RuntimeError):
@@ -191,6 +192,28 @@ def i8_dequant_dot(w: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, x_sc
     _check(_lib.loom_i8_dequant_dot(_ptr(w), _ptr(w_scale), _ptr(x), _ptr(x_scale), rows, 4 * kw, batch,
                                     _ptr(out), _ptr(acc), _stream(w)), "i8_dequant_dot")
     return (out, acc) if want_acc else out
+
+
+def packed_dot(fields: torch.Tensor, scales: torch.Tensor, rhs: torch.Tensor, count: int,
+               initial: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fields int32 [records][outputs], scales int16/uint16 binary16 bits [records][outputs],
+    rhs f32 [records][streams][4] -> out f32 [outputs] (the pages' ordered packed-dot recurrence)."""
+    _dev(fields, torch.int32, "fields")
+    if scales.dtype == torch.float16:
+        scales = scales.view(torch.int16)
+    if scales.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("scales must hold binary16 bit patterns (float16, int16 or uint16)")
+    _dev(rhs, torch.float32, "rhs")
+    assert fields.dim() == 2 and fields.is_contiguous() and scales.shape == fields.shape and scales.is_contiguous()
+    assert rhs.dim() == 3 and rhs.shape[2] == 4 and rhs.is_contiguous() and rhs.shape[0] >= count
+    records, outputs = fields.shape
+    if initial is not None:
+        _dev(initial, torch.float32, "initial")
+    if out is None:
+        out = torch.empty(outputs, dtype=torch.float32, device=fields.device)
+    _check(_lib.loom_packed_dot(_ptr(fields), _ptr(scales), _ptr(rhs), rhs.shape[1], _ptr(initial), records, count,
+                                outputs, _ptr(out), _stream(fields)), "packed_dot")
+    return out
 
 
 def pack_int8(t: torch.Tensor) -> torch.Tensor:

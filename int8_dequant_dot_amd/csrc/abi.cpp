@@ -110,3 +110,24 @@ extern "C" int loom_i8_dequant_dot(const int32_t *w, const float *w_scale, const
     return launch_status(loom::launch_i8_dequant_dot(cfg, w, w_scale, x, x_scale, (int)rows, (int)(k / 4),
                                                      (int)batch, out, acc, (hipStream_t)stream));
 }
+
+extern "C" int loom_packed_dot(const int32_t *fields, const uint16_t *scales, const float *rhs, int64_t streams,
+                               const float *initial, int64_t records, int64_t count, int64_t outputs, float *out,
+                               void *stream) {
+    if (records < 0 || count < 0 || count > records || count > kMaxRows || outputs < 0 || outputs > kMaxCopy ||
+        streams < 1 || streams > kMaxRows)
+        return LOOM_ERR_RANGE;
+    if (records > 0 && outputs > INT64_MAX / 4 / records) return LOOM_ERR_RANGE;
+    if (outputs == 0) return LOOM_OK;
+    if (!out || (count > 0 && (!fields || !scales || !rhs))) return LOOM_ERR_NULL;
+    if (misaligned(fields, 4) || misaligned(scales, 2) || misaligned(rhs, 16) || misaligned(initial, 4) ||
+        misaligned(out, 4))
+        return LOOM_ERR_ALIGN;
+    if (loom::packed_dot_outputs_per_lane(outputs, streams) == 4 && (misaligned(fields, 16) || misaligned(scales, 8)))
+        return LOOM_ERR_ALIGN;
+    loom_launch_config cfg;
+    const int64_t w[3] = {outputs, count, streams};
+    if (int st = loom::evaluate_launch(loom::kPackedDot, w, &cfg)) return st;
+    return launch_status(loom::launch_packed_dot(cfg, fields, scales, rhs, (int)streams, initial, (int)count,
+                                                 outputs, out, (hipStream_t)stream));
+}

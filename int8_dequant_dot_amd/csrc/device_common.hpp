@@ -13,6 +13,7 @@ constexpr int kWave = 64;          // gfx950 wavefront width
 
 typedef int   int4v   __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned uint2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 

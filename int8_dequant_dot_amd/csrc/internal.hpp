@@ -15,6 +15,7 @@ enum ExportId : uint32_t {
     kRowSums,
     kSegmentSums,
     kI8DequantDot,
+    kPackedDot,
     kExportCount
 };
 
@@ -49,6 +50,17 @@ constexpr int kMfmaTileRows = 16;
 constexpr int kMfmaKSplit = LOOM_MFMA_KSPLIT;
 constexpr bool kMfmaStage = LOOM_MFMA_STAGE != 0;
 constexpr uint32_t kMfmaStageBytes = 16 * 256;  // per wave: 16 rows x 256 B
+// Outputs per lane of the packed-dot recurrence: 4 once there are enough
+// outputs to fill the GPU with wide loads and the stream count keeps four
+// consecutive outputs on four consecutive streams; otherwise 1 (the pages'
+// one lane per output, best for the latency-bound small shapes).
+#ifndef LOOM_PACKED_DOT_WIDE_MIN
+#define LOOM_PACKED_DOT_WIDE_MIN 65536
+#endif
+constexpr int packed_dot_outputs_per_lane(int64_t outputs, int64_t streams) {
+    return (outputs >= LOOM_PACKED_DOT_WIDE_MIN && outputs % 4 == 0 && streams % 4 == 0) ? 4 : 1;
+}
+
 // 16-vector column tiles the MFMA kernel needs for a batch.
 constexpr int mfma_col_tiles(int64_t batch) { return batch <= 16 ? 1 : batch <= 32 ? 2 : 4; }
 constexpr int kMaxBatch = 64;
@@ -69,5 +81,9 @@ hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, in
 hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,
                                  const int32_t *x, const float *x_scale, int rows, int k_words,
                                  int batch, float *out, int32_t *acc, hipStream_t stream);
+
+hipError_t launch_packed_dot(const loom_launch_config &cfg, const int32_t *fields, const uint16_t *scales,
+                             const float *rhs, int streams, const float *initial, int count, int64_t outputs,
+                             float *out, hipStream_t stream);
 
 }  // namespace loom

@@ -70,6 +70,13 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
                    (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));
 }
 
+// packed_dot(outputs, count, streams): 256 lanes per workgroup, one output
+// per lane, or four for large output counts (see packed_dot_outputs_per_lane).
+int geo_packed_dot(const int64_t *w, loom_launch_config *c) {
+    if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
+    return set(c, ceil_div(w[0], 256 * packed_dot_outputs_per_lane(w[0], w[2])), 256, 0);
+}
+
 struct Export {
     const char *name;
     size_t arity;
@@ -82,6 +89,7 @@ const Export kExports[kExportCount] = {
     {"row_sums", 2, geo_row_sums},
     {"segment_sums", 2, geo_segment_sums},
     {"i8_dequant_dot", 3, geo_i8},
+    {"packed_dot", 3, geo_packed_dot},
 };
 
 }  // namespace

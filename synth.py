@@ -149,6 +149,7 @@ DENSE = Workload("row_sum_65536x4096", 3, "dense row sum 65536x4096 f32, uniform
 SEGMENTS = Workload("segment_sums_16384x256", 4, "16384 segments, lengths U{0..4096}, 256 f32 cols N(0,1)")
 GEMV = Workload("i8_dot_16384x8192", 5, "int8 16384x8192 weights, per-row scale, one int8 vector")
 BATCHED = Workload("i8_dot_28672x8192x8", 6, "int8 28672x8192 weights x 8 int8 vectors, row and vector scales")
+PACKED = Workload("packed_dot_2048x128", 7, "2048 outputs x 128 records: packed s8 words, f16 scales, 64 f32 streams")
 
 # stream ids
 S_VALUES, S_COUNT, S_INITIAL, S_LENGTHS, S_W, S_WSCALE, S_X, S_XSCALE = range(8)
@@ -208,3 +209,23 @@ def i8_matrix(seed, stream, rows, k, device="cpu"):
 def scales(seed, stream, start, count, device="cpu"):
     """Per-row or per-vector scales uniform in [1e-3, 1e-2]."""
     return uniform_range(seed, stream, start, count, 1e-3, 1e-2, device)
+
+
+def f16_scales(seed, stream, start, count, device="cpu") -> torch.Tensor:
+    """binary16 bit patterns (as int16) of positive scales 2**e * (1 + m/1024),
+    e uniform in {-10..-7}, m uniform in [0, 1024): values in [2**-10, 2**-6).
+    Built from integer draws only, so CPU and GPU give identical bits."""
+    z = _lshr(draws(seed, stream, start, count, device), 1)
+    e = torch.remainder(z, 4) - 10
+    m = torch.remainder(_lshr(z, 8), 1024)
+    return (((e + 15) << 10) | m).to(torch.int16)
+
+
+def packed_dot_inputs(seed=PACKED.seed, records=128, outputs=2048, streams=64, device="cpu"):
+    """fields int32 [records][outputs], scales binary16 bits [records][outputs],
+    rhs f32 [records][streams][4] N(0,1), initial f32 [outputs] N(0,1)."""
+    fields = _lshr(draws(seed, S_W, 0, records * outputs, device), 32).to(torch.int32).view(records, outputs)
+    scales = f16_scales(seed, S_WSCALE, 0, records * outputs, device).view(records, outputs)
+    rhs = normal(seed, S_X, 0, records * streams * 4, device).view(records, streams, 4)
+    initial = normal(seed, S_INITIAL, 0, outputs, device)
+    return fields, scales, rhs, initial

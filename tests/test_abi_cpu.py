@@ -207,3 +207,22 @@ def test_binding_refuses_cpu_tensors(loom):
         loom.row_sums(torch.zeros(4, 4))
     with pytest.raises(TypeError):
         loom.i8_dequant_dot(torch.zeros(4, 4, dtype=torch.int32), torch.zeros(4), torch.zeros(4, dtype=torch.int32))
+
+
+def test_packed_dot_validation(loom, lib):
+    f = lib.loom_packed_dot
+    # (fields, scales, rhs, streams, initial, records, count, outputs, out, stream)
+    assert f(FAKE, FAKE, FAKE, 64, None, 128, 129, 2048, FAKE, None) == loom.ERR_RANGE  # count > records
+    assert f(FAKE, FAKE, FAKE, 64, None, 128, -1, 2048, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, 0, None, 128, 8, 2048, FAKE, None) == loom.ERR_RANGE  # no streams
+    assert f(FAKE, FAKE, FAKE, 64, None, 128, 8, -1, FAKE, None) == loom.ERR_RANGE
+    assert f(None, None, None, 64, None, 128, 8, 0, None, None) == loom.OK
+    assert f(None, FAKE, FAKE, 64, None, 128, 8, 2048, FAKE, None) == loom.ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 64, None, 128, 8, 2048, None, None) == loom.ERR_NULL
+    assert f(FAKE, FAKE, FAKE + 4, 64, None, 128, 8, 2048, FAKE, None) == loom.ERR_ALIGN  # rhs needs 16 B
+    assert f(FAKE, FAKE + 1, FAKE, 64, None, 128, 8, 2048, FAKE, None) == loom.ERR_ALIGN
+    tok = loom.launch_config_lookup("packed_dot")
+    assert loom.launch_config_invoke(tok, [2048, 128, 64])["workgroups"] == (8, 1, 1)
+    assert loom.launch_config_invoke(tok, [262144, 128, 64])["workgroups"] == (256, 1, 1)  # 4 outputs per lane
+    assert loom.launch_config_invoke(tok, [262146, 128, 64])["workgroups"] == (1025, 1, 1)
+    assert loom.launch_config_invoke(tok, [2049, 0, 3])["workgroups"] == (9, 1, 1)

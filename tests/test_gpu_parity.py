@@ -343,3 +343,50 @@ def test_tile_workload(loom, device):
     osums, ofr, otc = oracle.row_sum_tiles(values.numpy(), count)
     assert (int(_np(fr)[0]), int(_np(tc)[0])) == (ofr, otc)
     assert_sum_close(_np(sums), osums, None, np.abs(values.numpy()[:ofr]).sum(), what="tile")
+
+
+# ------------------------------------------------------------------ packed dot (pages' literal form)
+
+PACKED_LENGTHS = [0, 1, 2, 3, 4, 5, 7, 8, 9, 15, 16, 17, 127, 128]  # 14 lengths, as on the page
+
+
+def _run_packed(loom, device, fields, scales, rhs, count, initial):
+    out = loom.packed_dot(fields.to(device), scales.to(device), rhs.to(device), count,
+                          None if initial is None else initial.to(device))
+    return _np(out)
+
+
+@pytest.mark.parametrize("count", PACKED_LENGTHS)
+def test_packed_dot_page_shape_bitwise(loom, device, count):
+    # 2048 outputs x up to 128 records, 64 shared streams: the GPU recurrence
+    # must equal the serial oracle bit for bit at every length
+    fields, scales, rhs, initial = synth.packed_dot_inputs()
+    g = _run_packed(loom, device, fields, scales, rhs, count, initial)
+    ref = oracle.packed_dot(fields.numpy(), scales.numpy(), rhs.numpy(), count, initial.numpy())[0]
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("outputs,streams,count", [(1, 1, 5), (100, 3, 17), (70001, 64, 9), (300, 100, 33),
+                                                   (64, 64, 128)])
+def test_packed_dot_odd_shapes_bitwise(loom, device, outputs, streams, count):
+    fields, scales, rhs, initial = synth.packed_dot_inputs(seed=70 + outputs, records=max(count, 1) + 2,
+                                                          outputs=outputs, streams=streams)
+    for init in (initial, None):
+        g = _run_packed(loom, device, fields, scales, rhs, count, init)
+        ref = oracle.packed_dot(fields.numpy(), scales.numpy(), rhs.numpy(), count,
+                                None if init is None else init.numpy())[0]
+        assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
+def test_packed_dot_large_sampled(loom, device):
+    records, outputs, streams = 128, 262144, 64
+    fields, scales, rhs, initial = synth.packed_dot_inputs(seed=77, records=records, outputs=outputs,
+                                                          streams=streams, device=device)
+    g = _np(loom.packed_dot(fields, scales, rhs, records, initial))
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([[0, outputs - 1], rng.integers(0, outputs, 200)]))
+    f, s, r, i = (t.cpu().numpy() for t in (fields, scales, rhs, initial))
+    # each sampled output keeps its own activation stream (o mod 64)
+    ref = np.array([oracle.packed_dot(f[:, [o]], s[:, [o]], r[:, [o % streams]], records, i[[o]])[0][0]
+                    for o in sample], np.float32)
+    assert np.array_equal(g[sample].view(np.uint32), ref.view(np.uint32))
