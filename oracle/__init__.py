@@ -53,6 +53,7 @@ def lib():
         l.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
         l.oracle_f16_to_f32.restype = ctypes.c_float
         l.oracle_packed_dot.argtypes = [p, p, p, i64, p, i64, i64, p, p, p]
+        l.oracle_sum_guarded_rows.argtypes = [p, i64, i64, i64, p]
         _lib = l
     return _lib
 
@@ -161,3 +162,13 @@ def packed_dot(fields, scales, rhs, count: int, initial=None, shadows: bool = Tr
     lib().oracle_packed_dot(_ptr(fields), _ptr(scales), _ptr(rhs), streams, _ptr(init), count, outputs,
                             _ptr(out), _ptr(d), _ptr(a))
     return out, d, a
+
+
+def sum_guarded_rows(values, count: int, columns: int, active_lanes: int):
+    """values f32 [rows_alloc][32][4] -> sums f32 [32] (the pages' guarded ragged row sum)."""
+    values = _arr(values, np.float32)
+    assert values.ndim == 3 and values.shape[1:] == (32, 4) and 0 <= count <= values.shape[0]
+    assert 0 <= columns <= 4 and 0 <= active_lanes <= 32
+    sums = np.empty(32, np.float32)
+    lib().oracle_sum_guarded_rows(_ptr(values), count, columns, active_lanes, _ptr(sums))
+    return sums

@@ -251,3 +251,37 @@ void oracle_packed_dot(const int32_t *fields, const uint16_t *scales, const floa
         if (out_abs) out_abs[o] = a;
     }
 }
+
+/* [TUNE] §Keep guards and inner loops in the source (@guide.sum_guarded_rows).
+ * values is a [rows_alloc][32][4] f32 tile.  The row range is rounded up to a
+ * multiple of 4; for every row of that padded range, in order, a lane's
+ * partial is 0 for rows at or beyond count (those rows, including the padded
+ * one, are never read); otherwise it is the inner sum, from 0, over the first
+ * `columns` components of values[row][lane][*] in order, each component 0
+ * for lanes at or beyond active_lanes (whose values are never read).  The
+ * partial is added to the lane's carried sum, which starts at 0. */
+void oracle_sum_guarded_rows(const float *values, int64_t count, int64_t columns, int64_t active_lanes,
+                             float *sums)
+{
+    const int64_t lanes = 32, tile_width = 4;
+    int64_t padded = count + (tile_width - 1);
+    int64_t end = (padded / tile_width) * tile_width;
+    for (int64_t lane = 0; lane < lanes; ++lane) {
+        float sum = 0.0f;
+        int active = lane < active_lanes;
+        for (int64_t row = 0; row < end; ++row) {
+            float partial = 0.0f;
+            if (row < count) {
+                float component_sum = 0.0f;
+                for (int64_t column = 0; column < columns; ++column) {
+                    float value = 0.0f;
+                    if (active) value = values[(row * lanes + lane) * 4 + column];
+                    component_sum = component_sum + value;
+                }
+                partial = component_sum;
+            }
+            sum = sum + partial;
+        }
+        sums[lane] = sum;
+    }
+}

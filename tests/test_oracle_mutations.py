@@ -35,6 +35,10 @@ MUTATIONS = {
                                   "int byte = (uint8_t)(word >> (8 * j));"),
     "packed-dot stream by division": ("int64_t stream = o % streams;", "int64_t stream = (o / streams) % streams;"),
     "packed-dot scale ignored": ("float v = (float)byte * scale;", "float v = (float)byte;"),
+    "guarded rows: inner loop one short": ("for (int64_t column = 0; column < columns; ++column) {",
+                                           "for (int64_t column = 0; column + 1 < columns; ++column) {"),
+    "guarded rows: lane guard ignored": ("if (active) value = values[", "value = values["),
+    "guarded rows: row guard off by one": ("if (row < count) {", "if (row <= count && row < 63) {"),
     "packed-dot byte order reversed": ("int8_t byte = (int8_t)(uint8_t)(word >> (8 * j));",
                                        "int8_t byte = (int8_t)(uint8_t)(word >> (8 * (3 - j)));"),
 }

@@ -443,3 +443,51 @@ def test_packed_dot_random_within_bound():
         # with the activation rounds once, then n recursive additions
         assert abs(Fraction(float(out[o])) - exact) <= gamma(n + 1) * absum
         assert abs(d[o] - float(exact)) <= gamma(n + 1, U64) * absum + 1e-300
+
+
+# ------------------------------------------------------------------ guarded ragged rows
+# TUNE §Keep guards and inner loops in the source (@guide.sum_guarded_rows)
+
+def _guarded_iota():
+    r = np.arange(63)[:, None, None]
+    l = np.arange(32)[None, :, None]
+    c = np.arange(4)[None, None, :]
+    return (1 + 4 * (32 * r + l) + c).astype(np.float32)
+
+
+def test_guarded_rows_closed_form():
+    # active lane l, N rows, C components: sum_r sum_c (1 + 128 r + 4 l + c)
+    #   = N C (1 + 4 l) + 64 C N (N - 1) + N C (C - 1) / 2; inactive lanes give 0
+    v = _guarded_iota()
+    lanes = np.arange(32)
+    for n in (0, 1, 2, 3, 4, 5, 8, 62, 63):
+        for cols in range(5):
+            for active in (0, 1, 17, 32):
+                out = oracle.sum_guarded_rows(v, n, cols, active)
+                want = n * cols * (1 + 4 * lanes) + 64 * cols * n * (n - 1) + n * cols * (cols - 1) // 2
+                want = np.where(lanes < active, want, 0).astype(np.float32)
+                assert np.array_equal(out, want), (n, cols, active)
+
+
+def test_guarded_rows_never_read_outside_guards():
+    rng = np.random.default_rng(6)
+    for n, cols, active in [(63, 4, 32), (5, 2, 17), (4, 3, 1), (1, 1, 31), (62, 4, 0)]:
+        v = rng.integers(-9, 10, size=(63, 32, 4)).astype(np.float32)
+        poisoned = v.copy()
+        poisoned[n:] = np.nan            # rows at or beyond count (the padded row is not even allocated)
+        poisoned[:, active:] = np.nan    # inactive lanes
+        poisoned[:, :, cols:] = np.nan   # components beyond the inner extent
+        a = oracle.sum_guarded_rows(v, n, cols, active)
+        b = oracle.sum_guarded_rows(poisoned, n, cols, active)
+        assert np.array_equal(a, b) and not np.any(np.isnan(b))
+        exact = v[:n, :, :cols].astype(np.int64).sum((0, 2))
+        assert np.array_equal(b, np.where(np.arange(32) < active, exact, 0).astype(np.float32))
+
+
+def test_guarded_rows_random_within_bound():
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((63, 32, 4)).astype(np.float32)
+    out = oracle.sum_guarded_rows(v, 63, 4, 32)
+    for lane in range(32):
+        terms = [float(t) for t in v[:, lane, :].ravel()]
+        assert abs(float(out[lane]) - math.fsum(terms)) <= gamma(len(terms) + 16) * math.fsum(abs(t) for t in terms)
