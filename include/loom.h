@@ -79,6 +79,7 @@ typedef struct loom_launch_config {
  *   "segment_sums"    (segments, cols)
  *   "i8_dequant_dot"  (rows, k, batch)
  *   "packed_dot"      (outputs, count, streams)
+ *   "sum_guarded_rows" (count)
  * lookup: LOOM_ERR_NULL if a pointer is NULL, LOOM_ERR_UNKNOWN_EXPORT if no
  * kernel has that name.  The token stays valid for the life of the process. */
 int loom_launch_config_lookup(const char *export_name, uint32_t *token);
@@ -210,6 +211,24 @@ int loom_i8_dequant_dot(const int32_t *w, const float *w_scale, const int32_t *x
 int loom_packed_dot(const int32_t *fields, const uint16_t *scales, const float *rhs, int64_t streams,
                     const float *initial, int64_t records, int64_t count, int64_t outputs, float *out,
                     void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * The pages' guarded ragged row sum (TUNE §Keep guards and inner loops in   *
+ * the source, @guide.sum_guarded_rows).  For each lane l < 32, rows are      *
+ * walked in order up to count rounded up to a multiple of 4; a row at or    *
+ * beyond count contributes 0 and is not read; otherwise its partial is the  *
+ * in-order f32 sum, from 0, of values[row][l][c] for c < columns, each      *
+ * taken as 0 (and not read) when l >= active_lanes.  sums[l] is the in-order *
+ * f32 sum of the partials, from 0 -- the serial recurrence bit for bit.     *
+ *   values       : f32[rows_alloc][32][4], 16-byte aligned                  *
+ *   rows_alloc   : 0 <= rows_alloc <= 2^26                                  *
+ *   count        : 0 <= count <= rows_alloc (the padded row need not exist) *
+ *   columns      : 0 <= columns <= 4                                        *
+ *   active_lanes : 0 <= active_lanes <= 32                                  *
+ *   sums         : f32[32]                                                  *
+ * ------------------------------------------------------------------------ */
+int loom_sum_guarded_rows(const float *values, int64_t rows_alloc, int64_t count, int64_t columns,
+                          int64_t active_lanes, float *sums, void *stream);
 
 #ifdef __cplusplus
 }

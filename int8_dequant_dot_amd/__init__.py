@@ -38,14 +38,17 @@ _lib.loom_row_sums.argtypes = [_p, _i64, _i64, _i64, _p, _p]
 _lib.loom_segment_sums.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p, _p]
 _lib.loom_i8_dequant_dot.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p]
 _lib.loom_packed_dot.argtypes = [_p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _p]
+_lib.loom_sum_guarded_rows.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _p]
 for _name in ("loom_launch_config_lookup", "loom_launch_config_invoke", "loom_copy_f32", "loom_row_sum_tiles",
-              "loom_row_sums", "loom_segment_sums", "loom_i8_dequant_dot", "loom_packed_dot"):
+              "loom_row_sums", "loom_segment_sums", "loom_i8_dequant_dot", "loom_packed_dot",
+              "loom_sum_guarded_rows"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 # status codes (include/loom.h)
 OK, ERR_NULL, ERR_RANGE, ERR_ALIGN, ERR_SHAPE, ERR_UNKNOWN_EXPORT, ERR_TOKEN, ERR_DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 
-EXPORTS = ("copy_f32", "row_sum_tiles", "row_sums", "segment_sums", "i8_dequant_dot", "packed_dot")
+EXPORTS = ("copy_f32", "row_sum_tiles", "row_sums", "segment_sums", "i8_dequant_dot", "packed_dot",
+           "sum_guarded_rows")
 
 
 class LoomError(RuntimeError):
@@ -213,6 +216,18 @@ def packed_dot(fields: torch.Tensor, scales: torch.Tensor, rhs: torch.Tensor, co
         out = torch.empty(outputs, dtype=torch.float32, device=fields.device)
     _check(_lib.loom_packed_dot(_ptr(fields), _ptr(scales), _ptr(rhs), rhs.shape[1], _ptr(initial), records, count,
                                 outputs, _ptr(out), _stream(fields)), "packed_dot")
+    return out
+
+
+def sum_guarded_rows(values: torch.Tensor, count: int, columns: int, active_lanes: int,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """values f32 [rows_alloc][32][4] -> sums f32 [32] (the pages' guarded ragged row sum)."""
+    _dev(values, torch.float32, "values")
+    assert values.dim() == 3 and tuple(values.shape[1:]) == (32, 4) and values.is_contiguous()
+    if out is None:
+        out = torch.empty(32, dtype=torch.float32, device=values.device)
+    _check(_lib.loom_sum_guarded_rows(_ptr(values), values.shape[0], count, columns, active_lanes, _ptr(out),
+                                      _stream(values)), "sum_guarded_rows")
     return out
 
 

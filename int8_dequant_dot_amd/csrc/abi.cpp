@@ -131,3 +131,17 @@ extern "C" int loom_packed_dot(const int32_t *fields, const uint16_t *scales, co
     return launch_status(loom::launch_packed_dot(cfg, fields, scales, rhs, (int)streams, initial, (int)count,
                                                  outputs, out, (hipStream_t)stream));
 }
+
+extern "C" int loom_sum_guarded_rows(const float *values, int64_t rows_alloc, int64_t count, int64_t columns,
+                                     int64_t active_lanes, float *sums, void *stream) {
+    if (rows_alloc < 0 || rows_alloc > kMaxTileRows || count < 0 || count > rows_alloc || columns < 0 ||
+        columns > 4 || active_lanes < 0 || active_lanes > 32)
+        return LOOM_ERR_RANGE;
+    if (!sums || (!values && rows_alloc > 0)) return LOOM_ERR_NULL;
+    if (misaligned(values, 16) || misaligned(sums, 4)) return LOOM_ERR_ALIGN;
+    loom_launch_config cfg;
+    const int64_t w[1] = {count};
+    if (int st = loom::evaluate_launch(loom::kSumGuardedRows, w, &cfg)) return st;
+    return launch_status(loom::launch_sum_guarded_rows(cfg, values, (int)count, (int)columns, (int)active_lanes,
+                                                       sums, (hipStream_t)stream));
+}

@@ -16,6 +16,7 @@ enum ExportId : uint32_t {
     kSegmentSums,
     kI8DequantDot,
     kPackedDot,
+    kSumGuardedRows,
     kExportCount
 };
 
@@ -85,5 +86,8 @@ hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w
 hipError_t launch_packed_dot(const loom_launch_config &cfg, const int32_t *fields, const uint16_t *scales,
                              const float *rhs, int streams, const float *initial, int count, int64_t outputs,
                              float *out, hipStream_t stream);
+
+hipError_t launch_sum_guarded_rows(const loom_launch_config &cfg, const float *values, int count, int columns,
+                                   int active_lanes, float *sums, hipStream_t stream);
 
 }  // namespace loom

@@ -77,6 +77,12 @@ int geo_packed_dot(const int64_t *w, loom_launch_config *c) {
     return set(c, ceil_div(w[0], 256 * packed_dot_outputs_per_lane(w[0], w[2])), 256, 0);
 }
 
+// sum_guarded_rows(count): one workgroup of 32 work-items, one per tile lane.
+int geo_sum_guarded_rows(const int64_t *w, loom_launch_config *c) {
+    if (w[0] < 0) return LOOM_ERR_RANGE;
+    return set(c, 1, 32, 0);
+}
+
 struct Export {
     const char *name;
     size_t arity;
@@ -90,6 +96,7 @@ const Export kExports[kExportCount] = {
     {"segment_sums", 2, geo_segment_sums},
     {"i8_dequant_dot", 3, geo_i8},
     {"packed_dot", 3, geo_packed_dot},
+    {"sum_guarded_rows", 1, geo_sum_guarded_rows},
 };
 
 }  // namespace

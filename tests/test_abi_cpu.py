@@ -226,3 +226,17 @@ def test_packed_dot_validation(loom, lib):
     assert loom.launch_config_invoke(tok, [262144, 128, 64])["workgroups"] == (256, 1, 1)  # 4 outputs per lane
     assert loom.launch_config_invoke(tok, [262146, 128, 64])["workgroups"] == (1025, 1, 1)
     assert loom.launch_config_invoke(tok, [2049, 0, 3])["workgroups"] == (9, 1, 1)
+
+
+def test_sum_guarded_rows_validation(loom, lib):
+    f = lib.loom_sum_guarded_rows
+    assert f(FAKE, 63, 64, 4, 32, FAKE, None) == loom.ERR_RANGE  # count > rows_alloc
+    assert f(FAKE, 63, 8, 5, 32, FAKE, None) == loom.ERR_RANGE   # at most 4 components
+    assert f(FAKE, 63, 8, 4, 33, FAKE, None) == loom.ERR_RANGE   # at most 32 lanes
+    assert f(FAKE, 63, 8, -1, 32, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, 63, 8, 4, 32, None, None) == loom.ERR_NULL
+    assert f(None, 63, 8, 4, 32, FAKE, None) == loom.ERR_NULL
+    assert f(FAKE + 4, 63, 8, 4, 32, FAKE, None) == loom.ERR_ALIGN
+    tok = loom.launch_config_lookup("sum_guarded_rows")
+    cfg = loom.launch_config_invoke(tok, [63])
+    assert cfg["workgroups"] == (1, 1, 1) and cfg["workgroup_size"] == (32, 1, 1)

@@ -390,3 +390,36 @@ def test_packed_dot_large_sampled(loom, device):
     ref = np.array([oracle.packed_dot(f[:, [o]], s[:, [o]], r[:, [o % streams]], records, i[[o]])[0][0]
                     for o in sample], np.float32)
     assert np.array_equal(g[sample].view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ guarded ragged rows (pages' motif)
+
+def test_sum_guarded_rows_360_combinations_bitwise(loom, device):
+    # mixed-sign inputs, bit for bit, across 6 row counts x 5 inner extents x
+    # 4 active-lane counts x 3 seeds = 360 combinations; each allocation ends
+    # at `count` rows, so the padded row never exists
+    n = 0
+    for seed in (1, 2, 3):
+        full = synth.normal(seed, synth.S_VALUES, 0, 63 * 32 * 4).view(63, 32, 4)
+        for count in (0, 1, 3, 4, 5, 63):
+            v = full[:count].contiguous()
+            dv = v.to(device) if count else torch.zeros((0, 32, 4), device=device)
+            for columns in range(5):
+                for active in (0, 1, 17, 32):
+                    g = _np(loom.sum_guarded_rows(dv, count, columns, active))
+                    ref = oracle.sum_guarded_rows(full.numpy(), count, columns, active)
+                    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32)), (seed, count, columns, active)
+                    n += 1
+    assert n == 360
+
+
+def test_sum_guarded_rows_poisoned(loom, device):
+    # NaN in every element the guards exclude must not reach the sums
+    v = synth.normal(9, synth.S_VALUES, 0, 63 * 32 * 4).view(63, 32, 4).numpy().copy()
+    for count, columns, active in [(63, 2, 17), (5, 3, 31), (62, 1, 1)]:
+        p = v.copy()
+        p[count:] = np.nan
+        p[:, active:] = np.nan
+        p[:, :, columns:] = np.nan
+        g = _np(loom.sum_guarded_rows(torch.from_numpy(p).to(device), count, columns, active))
+        assert np.array_equal(g.view(np.uint32), oracle.sum_guarded_rows(v, count, columns, active).view(np.uint32))
