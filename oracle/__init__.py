@@ -54,6 +54,7 @@ def lib():
         l.oracle_f16_to_f32.restype = ctypes.c_float
         l.oracle_packed_dot.argtypes = [p, p, p, i64, p, i64, i64, p, p, p]
         l.oracle_sum_guarded_rows.argtypes = [p, i64, i64, i64, p]
+        l.oracle_routed_combine.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p]
         _lib = l
     return _lib
 
@@ -172,3 +173,20 @@ def sum_guarded_rows(values, count: int, columns: int, active_lanes: int):
     sums = np.empty(32, np.float32)
     lib().oracle_sum_guarded_rows(_ptr(values), count, columns, active_lanes, _ptr(sums))
     return sums
+
+
+def routed_combine(ids, weights, payload, shadows: bool = True):
+    """ids int32 [tokens][routes], weights f32 [tokens][routes], payload f32 [num_rows][hidden]
+    -> (out f32 [tokens][hidden], out_f64, sum |terms|)."""
+    ids = _arr(ids, np.int32)
+    weights = _arr(weights, np.float32)
+    payload = _arr(payload, np.float32)
+    tokens, routes = ids.shape
+    num_rows, hidden = payload.shape
+    assert weights.shape == ids.shape
+    out = np.empty((tokens, hidden), np.float32)
+    d = np.empty((tokens, hidden), np.float64) if shadows else None
+    a = np.empty((tokens, hidden), np.float64) if shadows else None
+    lib().oracle_routed_combine(_ptr(ids), _ptr(weights), _ptr(payload), num_rows, tokens, routes, hidden,
+                                _ptr(out), _ptr(d), _ptr(a))
+    return out, d, a

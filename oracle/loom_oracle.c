@@ -285,3 +285,35 @@ void oracle_sum_guarded_rows(const float *values, int64_t count, int64_t columns
         sums[lane] = sum;
     }
 }
+
+/* [TUNE] §Separate route and payload lookahead (the routed MoE combine): for
+ * token t, each route i < routes in order carries a row id and a weight.  A
+ * route whose id lies outside [0, num_rows) -- compared as unsigned, so
+ * negative ids are outside -- is missing: neither its weight nor its payload
+ * row is read and the sum is unchanged.  Otherwise, for every column c,
+ *     acc[c] = acc[c] + weights[t][i] * payload[id][c]
+ * (the product rounded, then the sum), starting from 0; out[t][c] = acc[c]. */
+void oracle_routed_combine(const int32_t *ids, const float *weights, const float *payload, int64_t num_rows,
+                           int64_t tokens, int64_t routes, int64_t hidden, float *out, double *out_f64,
+                           double *out_abs)
+{
+    for (int64_t t = 0; t < tokens; ++t) {
+        for (int64_t c = 0; c < hidden; ++c) {
+            float acc = 0.0f;
+            double d = 0.0, a = 0.0;
+            for (int64_t i = 0; i < routes; ++i) {
+                uint32_t id = (uint32_t)ids[t * routes + i];
+                if ((uint64_t)id >= (uint64_t)num_rows) continue;
+                float w = weights[t * routes + i];
+                float p = payload[(int64_t)id * hidden + c];
+                float product = w * p;
+                acc = acc + product;
+                d = d + (double)w * (double)p;
+                a = a + fabs((double)w * (double)p);
+            }
+            out[t * hidden + c] = acc;
+            if (out_f64) out_f64[t * hidden + c] = d;
+            if (out_abs) out_abs[t * hidden + c] = a;
+        }
+    }
+}

@@ -39,6 +39,12 @@ MUTATIONS = {
                                            "for (int64_t column = 0; column + 1 < columns; ++column) {"),
     "guarded rows: lane guard ignored": ("if (active) value = values[", "value = values["),
     "guarded rows: row guard off by one": ("if (row < count) {", "if (row <= count && row < 63) {"),
+    "routed combine: signed id check": ("if ((uint64_t)id >= (uint64_t)num_rows) continue;",
+                                        "if ((int32_t)id >= num_rows) continue; if ((int32_t)id < 0) id = 0;"),
+    "routed combine: last row treated as missing": ("if ((uint64_t)id >= (uint64_t)num_rows) continue;",
+                                                    "if ((uint64_t)id + 1 >= (uint64_t)num_rows) continue;"),
+    "routed combine: weight of the wrong route": ("float w = weights[t * routes + i];",
+                                                 "float w = weights[t * routes + (i + 1) % routes];"),
     "packed-dot byte order reversed": ("int8_t byte = (int8_t)(uint8_t)(word >> (8 * j));",
                                        "int8_t byte = (int8_t)(uint8_t)(word >> (8 * (3 - j)));"),
 }

@@ -491,3 +491,67 @@ def test_guarded_rows_random_within_bound():
     for lane in range(32):
         terms = [float(t) for t in v[:, lane, :].ravel()]
         assert abs(float(out[lane]) - math.fsum(terms)) <= gamma(len(terms) + 16) * math.fsum(abs(t) for t in terms)
+
+
+# ------------------------------------------------------------------ routed row combine
+# TUNE §Separate route and payload lookahead
+
+def test_routed_combine_missing_routes_read_nothing():
+    rng = np.random.default_rng(8)
+    tokens, routes, num_rows, hidden = 7, 8, 20, 12
+    payload = rng.integers(-5, 6, size=(num_rows, hidden)).astype(np.float32)
+    ids = rng.integers(0, num_rows, size=(tokens, routes)).astype(np.int32)
+    weights = rng.integers(-3, 4, size=(tokens, routes)).astype(np.float32)
+    missing = rng.random((tokens, routes)) < 0.4
+    ids[missing] = np.where(rng.random(missing.sum()) < 0.5, -1 - rng.integers(0, 5, missing.sum()),
+                            num_rows + rng.integers(0, 5, missing.sum()))
+    ids[0, 0], ids[0, 1] = -(2 ** 31), num_rows   # extremes of both sides
+    missing[0, :2] = True
+    weights[missing] = np.nan                      # must never be read
+    out = oracle.routed_combine(ids, weights, payload)[0]
+    # exact integer reference over the valid routes
+    ref = np.zeros((tokens, hidden), np.int64)
+    for t in range(tokens):
+        for i in range(routes):
+            if not missing[t, i]:
+                ref[t] += int(weights[t, i]) * payload[ids[t, i]].astype(np.int64)
+    assert np.array_equal(out, ref.astype(np.float32))
+
+
+def test_routed_combine_single_route_copies_row():
+    rng = np.random.default_rng(9)
+    payload = rng.standard_normal((30, 17)).astype(np.float32)
+    ids = np.full((5, 4), -1, np.int32)
+    weights = np.zeros((5, 4), np.float32)
+    for t in range(5):
+        ids[t, t % 4] = 3 * t + 1
+        weights[t, t % 4] = 1.0
+    out = oracle.routed_combine(ids, weights, payload)[0]
+    assert np.array_equal(out, payload[[1, 4, 7, 10, 13]])
+    assert np.all(oracle.routed_combine(np.full((2, 3), -7, np.int32), np.ones((2, 3), np.float32), payload)[0] == 0)
+
+
+def test_routed_combine_duplicates_and_order():
+    # the same row twice contributes twice; routes are added in order, one at a
+    # time: 2^24 followed by two 1's stays 2^24 in f32
+    payload = np.array([[2.0 ** 24], [1.0]], np.float32)
+    out = oracle.routed_combine(np.array([[0, 1, 1]], np.int32), np.ones((1, 3), np.float32), payload)[0]
+    assert out[0, 0] == np.float32(2.0 ** 24)
+    out = oracle.routed_combine(np.array([[1, 1, 1]], np.int32), np.array([[2, 3, 4]], np.float32), payload)[0]
+    assert out[0, 0] == 9.0
+
+
+def test_routed_combine_random_within_bound():
+    rng = np.random.default_rng(10)
+    tokens, routes, num_rows, hidden = 6, 32, 64, 9
+    payload = rng.standard_normal((num_rows, hidden)).astype(np.float32)
+    ids = rng.integers(-4, num_rows + 4, size=(tokens, routes)).astype(np.int32)
+    weights = rng.random((tokens, routes)).astype(np.float32)
+    out, d, a = oracle.routed_combine(ids, weights, payload)
+    for t in range(tokens):
+        valid = [i for i in range(routes) if 0 <= ids[t, i] < num_rows]
+        for c in range(hidden):
+            terms = [Fraction(float(weights[t, i])) * Fraction(float(payload[ids[t, i], c])) for i in valid]
+            exact = sum(terms, Fraction(0))
+            absum = float(sum(abs(x) for x in terms))
+            assert abs(Fraction(float(out[t, c])) - exact) <= gamma(len(valid) + 1) * absum
