@@ -209,6 +209,27 @@ def main():
         parts[label] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                         "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    # Routed row combine: the pages' n8/n32 shapes (1024-wide rows, latency-
+    # bound) and a large one (16384 tokens x 8 routes) for bandwidth.
+    for label, tokens, routes in (("routed_combine_n8_t256", 256, 8), ("routed_combine_n32_t256", 256, 32),
+                                  ("routed_combine_n8_t16384", 16384, 8)):
+        rid, rw, rp = synth.routed_inputs(tokens=tokens, routes=routes, hidden=1024, device=dev)
+        rout = torch.empty(tokens, 1024, device=dev)
+        valid = int(((rid >= 0) & (rid < rp.shape[0])).sum().item())
+        nbytes = valid * (1024 * 4 + 4) + rid.numel() * 4 + tokens * 1024 * 4
+        loom.routed_combine(rid, rw, rp, out=rout)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(K):
+            loom.routed_combine(rid, rw, rp, out=rout)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        parts[label] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del rid, rw, rp, rout
+
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- roofline of the dominant kernel

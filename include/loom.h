@@ -80,6 +80,7 @@ typedef struct loom_launch_config {
  *   "i8_dequant_dot"  (rows, k, batch)
  *   "packed_dot"      (outputs, count, streams)
  *   "sum_guarded_rows" (count)
+ *   "routed_combine"  (tokens, routes, hidden)
  * lookup: LOOM_ERR_NULL if a pointer is NULL, LOOM_ERR_UNKNOWN_EXPORT if no
  * kernel has that name.  The token stays valid for the life of the process. */
 int loom_launch_config_lookup(const char *export_name, uint32_t *token);
@@ -229,6 +230,25 @@ int loom_packed_dot(const int32_t *fields, const uint16_t *scales, const float *
  * ------------------------------------------------------------------------ */
 int loom_sum_guarded_rows(const float *values, int64_t rows_alloc, int64_t count, int64_t columns,
                           int64_t active_lanes, float *sums, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * Routed row combine (TUNE §Separate route and payload lookahead: a routed  *
+ * MoE combine).  For token t and column c, routes i < routes in order:      *
+ *     id = ids[t][i]; if (uint32)id < num_rows:                             *
+ *         acc[c] = acc[c] + weights[t][i] * payload[id][c]                  *
+ * (product rounded, then added; acc starts at 0); out[t][c] = acc[c].  A   *
+ * route whose id is outside [0, num_rows) is missing: neither its weight    *
+ * nor its payload row is read.                                              *
+ *   ids     : int32[tokens][routes]                                         *
+ *   weights : f32[tokens][routes]                                           *
+ *   payload : f32[num_rows][hidden] expert-output rows, 16-byte aligned     *
+ *   num_rows: 0 <= num_rows < 2^31                                          *
+ *   tokens  : 0 <= tokens < 2^31; routes, hidden: 0 .. 2^20                 *
+ *   hidden  : a multiple of 4 (LOOM_ERR_SHAPE otherwise)                    *
+ *   out     : f32[tokens][hidden], 16-byte aligned                          *
+ * ------------------------------------------------------------------------ */
+int loom_routed_combine(const int32_t *ids, const float *weights, const float *payload, int64_t num_rows,
+                        int64_t tokens, int64_t routes, int64_t hidden, float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -39,16 +39,17 @@ _lib.loom_segment_sums.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p, _p]
 _lib.loom_i8_dequant_dot.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p]
 _lib.loom_packed_dot.argtypes = [_p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _p]
 _lib.loom_sum_guarded_rows.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _p]
+_lib.loom_routed_combine.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]
 for _name in ("loom_launch_config_lookup", "loom_launch_config_invoke", "loom_copy_f32", "loom_row_sum_tiles",
               "loom_row_sums", "loom_segment_sums", "loom_i8_dequant_dot", "loom_packed_dot",
-              "loom_sum_guarded_rows"):
+              "loom_sum_guarded_rows", "loom_routed_combine"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 # status codes (include/loom.h)
 OK, ERR_NULL, ERR_RANGE, ERR_ALIGN, ERR_SHAPE, ERR_UNKNOWN_EXPORT, ERR_TOKEN, ERR_DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 
 EXPORTS = ("copy_f32", "row_sum_tiles", "row_sums", "segment_sums", "i8_dequant_dot", "packed_dot",
-           "sum_guarded_rows")
+           "sum_guarded_rows", "routed_combine")
 
 
 class LoomError(RuntimeError):
@@ -228,6 +229,24 @@ def sum_guarded_rows(values: torch.Tensor, count: int, columns: int, active_lane
         out = torch.empty(32, dtype=torch.float32, device=values.device)
     _check(_lib.loom_sum_guarded_rows(_ptr(values), values.shape[0], count, columns, active_lanes, _ptr(out),
                                       _stream(values)), "sum_guarded_rows")
+    return out
+
+
+def routed_combine(ids: torch.Tensor, weights: torch.Tensor, payload: torch.Tensor,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """ids int32 [tokens][routes], weights f32 [tokens][routes], payload f32 [num_rows][hidden]
+    -> out f32 [tokens][hidden] (routed MoE combine; out-of-range ids are missing routes)."""
+    _dev(ids, torch.int32, "ids")
+    _dev(weights, torch.float32, "weights")
+    _dev(payload, torch.float32, "payload")
+    assert ids.dim() == 2 and ids.is_contiguous() and weights.shape == ids.shape and weights.is_contiguous()
+    assert payload.dim() == 2 and payload.is_contiguous()
+    tokens, routes = ids.shape
+    num_rows, hidden = payload.shape
+    if out is None:
+        out = torch.empty(tokens, hidden, dtype=torch.float32, device=ids.device)
+    _check(_lib.loom_routed_combine(_ptr(ids), _ptr(weights), _ptr(payload), num_rows, tokens, routes, hidden,
+                                    _ptr(out), _stream(ids)), "routed_combine")
     return out
 
 

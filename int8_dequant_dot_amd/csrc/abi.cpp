@@ -145,3 +145,20 @@ extern "C" int loom_sum_guarded_rows(const float *values, int64_t rows_alloc, in
     return launch_status(loom::launch_sum_guarded_rows(cfg, values, (int)count, (int)columns, (int)active_lanes,
                                                        sums, (hipStream_t)stream));
 }
+
+extern "C" int loom_routed_combine(const int32_t *ids, const float *weights, const float *payload, int64_t num_rows,
+                                   int64_t tokens, int64_t routes, int64_t hidden, float *out, void *stream) {
+    if (tokens < 0 || tokens > kMaxRows || routes < 0 || routes > (int64_t(1) << 20) || hidden < 0 ||
+        hidden > (int64_t(1) << 20) || num_rows < 0 || num_rows > kMaxRows)
+        return LOOM_ERR_RANGE;
+    if (hidden % 4 != 0) return LOOM_ERR_SHAPE;
+    if (tokens == 0 || hidden == 0) return LOOM_OK;
+    if (!out || (routes > 0 && (!ids || !weights)) || (num_rows > 0 && !payload)) return LOOM_ERR_NULL;
+    if (misaligned(ids, 4) || misaligned(weights, 4) || misaligned(payload, 16) || misaligned(out, 16))
+        return LOOM_ERR_ALIGN;
+    loom_launch_config cfg;
+    const int64_t w[3] = {tokens, routes, hidden};
+    if (int st = loom::evaluate_launch(loom::kRoutedCombine, w, &cfg)) return st;
+    return launch_status(loom::launch_routed_combine(cfg, ids, weights, payload, num_rows, (int)routes, (int)hidden,
+                                                     out, (hipStream_t)stream));
+}

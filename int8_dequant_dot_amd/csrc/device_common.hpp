@@ -89,9 +89,11 @@ __device__ __forceinline__ T wave_sum(T v) {
 //               exactly n times, in order.
 //
 // DEPTH-1 records stay in flight ahead of the consumer.  Loops of at least
-// 2*DEPTH-1 records take the pipelined path: an unconditional startup issues
+// DEPTH-1 records take the pipelined path: an unconditional startup issues
 // DEPTH-1 loads, the steady body (unrolled by DEPTH) issues one load and
-// consumes the oldest record per step, and the drain consumes the rest.  The
+// consumes the oldest record per step while at least 2*DEPTH-1 records
+// remain, and the drain consumes the last DEPTH-1 .. 2*DEPTH-2 records,
+// issuing the loads still missing.  The
 // ring rotates by renaming, never by copying -- a slot receives its next load
 // right after its old value was consumed -- and every path into the steady
 // loop has issued the same loads in the same order, so the compiler keeps
@@ -99,11 +101,11 @@ __device__ __forceinline__ T wave_sum(T v) {
 // across the backedge).  A scheduling fence (CTRL §Control instruction
 // order: it orders instructions without waiting for loads) after each step's
 // load keeps the compiler from sinking future loads below older consumer work
-// such as LDS staging.  Shorter loops run serially; an empty loop issues no
-// load.
+// such as LDS staging.  Loops shorter than DEPTH-1 run serially; an empty
+// loop issues no load.
 template <int DEPTH, typename T, typename N, typename Load, typename Consume>
 __device__ __forceinline__ void pipelined(N n, Load&& load, Consume&& consume) {
-    if (DEPTH <= 1 || n < 2 * DEPTH - 1) {
+    if (DEPTH <= 1 || n < DEPTH - 1) {
         for (N i = 0; i < n; ++i) {
             T v = load();
             consume(v);
@@ -123,7 +125,8 @@ __device__ __forceinline__ void pipelined(N n, Load&& load, Consume&& consume) {
                 consume(ring[j]);
             }
         }
-        // DEPTH-1 <= n - i <= 2*DEPTH-2 records remain, DEPTH-1 of them loaded.
+        // DEPTH-1 <= n - i <= 2*DEPTH-2 records remain, DEPTH-1 of them loaded
+        // (also when the steady loop ran zero times: then n - i = n).
         const int rest = (int)(n - i);
 #pragma unroll
         for (int j = 0; j < 2 * DEPTH - 1; ++j) {

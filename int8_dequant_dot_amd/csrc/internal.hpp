@@ -17,6 +17,7 @@ enum ExportId : uint32_t {
     kI8DequantDot,
     kPackedDot,
     kSumGuardedRows,
+    kRoutedCombine,
     kExportCount
 };
 
@@ -89,5 +90,9 @@ hipError_t launch_packed_dot(const loom_launch_config &cfg, const int32_t *field
 
 hipError_t launch_sum_guarded_rows(const loom_launch_config &cfg, const float *values, int count, int columns,
                                    int active_lanes, float *sums, hipStream_t stream);
+
+hipError_t launch_routed_combine(const loom_launch_config &cfg, const int32_t *ids, const float *weights,
+                                 const float *payload, int64_t num_rows, int routes, int hidden, float *out,
+                                 hipStream_t stream);
 
 }  // namespace loom

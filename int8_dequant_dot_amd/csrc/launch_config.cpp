@@ -33,6 +33,13 @@ int set(loom_launch_config *c, int64_t workgroups, uint32_t workgroup_size, uint
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int set2(loom_launch_config *c, int64_t gx, int64_t gy, uint32_t workgroup_size, uint32_t storage) {
+    if (gy < 0 || gy > 0xFFFF) return LOOM_ERR_RANGE;
+    const int st = set(c, gx, workgroup_size, storage);
+    if (st == LOOM_OK) c->workgroups[1] = (uint32_t)gy;
+    return st;
+}
+
 // copy_f32(n): one element per work-item, 256 per workgroup; 1009 -> 4.
 int geo_copy(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0) return LOOM_ERR_RANGE;
@@ -83,6 +90,12 @@ int geo_sum_guarded_rows(const int64_t *w, loom_launch_config *c) {
     return set(c, 1, 32, 0);
 }
 
+// routed_combine(tokens, routes, hidden): one wave per token and 256-column block.
+int geo_routed_combine(const int64_t *w, loom_launch_config *c) {
+    if (w[0] < 0 || w[1] < 0 || w[2] < 0) return LOOM_ERR_RANGE;
+    return set2(c, w[0], ceil_div(w[2], 256), kSubgroupSize, 0);
+}
+
 struct Export {
     const char *name;
     size_t arity;
@@ -97,6 +110,7 @@ const Export kExports[kExportCount] = {
     {"i8_dequant_dot", 3, geo_i8},
     {"packed_dot", 3, geo_packed_dot},
     {"sum_guarded_rows", 1, geo_sum_guarded_rows},
+    {"routed_combine", 3, geo_routed_combine},
 };
 
 }  // namespace

@@ -150,6 +150,7 @@ SEGMENTS = Workload("segment_sums_16384x256", 4, "16384 segments, lengths U{0..4
 GEMV = Workload("i8_dot_16384x8192", 5, "int8 16384x8192 weights, per-row scale, one int8 vector")
 BATCHED = Workload("i8_dot_28672x8192x8", 6, "int8 28672x8192 weights x 8 int8 vectors, row and vector scales")
 PACKED = Workload("packed_dot_2048x128", 7, "2048 outputs x 128 records: packed s8 words, f16 scales, 64 f32 streams")
+ROUTED = Workload("routed_combine", 8, "tokens x routes of (row id, weight) over expert-output rows of 1024 f32")
 
 # stream ids
 S_VALUES, S_COUNT, S_INITIAL, S_LENGTHS, S_W, S_WSCALE, S_X, S_XSCALE = range(8)
@@ -229,3 +230,20 @@ def packed_dot_inputs(seed=PACKED.seed, records=128, outputs=2048, streams=64, d
     rhs = normal(seed, S_X, 0, records * streams * 4, device).view(records, streams, 4)
     initial = normal(seed, S_INITIAL, 0, outputs, device)
     return fields, scales, rhs, initial
+
+
+def routed_inputs(seed=ROUTED.seed, tokens=256, routes=8, hidden=1024, missing_percent=5, device="cpu"):
+    """ids int32 [tokens][routes] uniform over num_rows = tokens * routes expert-output rows,
+    missing_percent of them replaced by an out-of-range id (alternately -1 and num_rows + k);
+    weights f32 [tokens][routes] uniform [1e-3, 1e-2); payload f32 [num_rows][hidden] N(0,1)."""
+    num_rows = tokens * routes
+    n = tokens * routes
+    ids = randint(seed, S_LENGTHS, 0, n, 0, num_rows - 1, device)
+    miss = randint(seed, S_COUNT, 0, n, 0, 99, device) < missing_percent
+    odd = randint(seed, S_INITIAL, 0, n, 0, 1, device) == 1
+    bad = torch.where(odd, torch.full_like(ids, -1), num_rows + randint(seed, S_XSCALE, 0, n, 0, 1000, device))
+    ids = torch.where(miss, bad, ids).to(torch.int32).view(tokens, routes)
+    weights = scales(seed, S_WSCALE, 0, n, device).view(tokens, routes)
+    payload = torch.empty(num_rows, hidden, dtype=torch.float32, device=device)
+    fill_chunked(payload, normal, seed, S_VALUES)
+    return ids, weights, payload

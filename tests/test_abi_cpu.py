@@ -240,3 +240,21 @@ def test_sum_guarded_rows_validation(loom, lib):
     tok = loom.launch_config_lookup("sum_guarded_rows")
     cfg = loom.launch_config_invoke(tok, [63])
     assert cfg["workgroups"] == (1, 1, 1) and cfg["workgroup_size"] == (32, 1, 1)
+
+
+def test_routed_combine_validation(loom, lib):
+    f = lib.loom_routed_combine
+    # (ids, weights, payload, num_rows, tokens, routes, hidden, out, stream)
+    assert f(FAKE, FAKE, FAKE, 10, -1, 8, 64, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, -1, 4, 8, 64, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, 10, 4, (1 << 20) + 1, 64, FAKE, None) == loom.ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, 10, 4, 8, 66, FAKE, None) == loom.ERR_SHAPE  # hidden % 4
+    assert f(None, None, None, 10, 0, 8, 64, None, None) == loom.OK
+    assert f(None, FAKE, FAKE, 10, 4, 8, 64, FAKE, None) == loom.ERR_NULL
+    assert f(FAKE, FAKE, None, 10, 4, 8, 64, FAKE, None) == loom.ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 10, 4, 8, 64, None, None) == loom.ERR_NULL
+    assert f(FAKE, FAKE, FAKE + 4, 10, 4, 8, 64, FAKE, None) == loom.ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, 10, 4, 8, 64, FAKE + 8, None) == loom.ERR_ALIGN
+    tok = loom.launch_config_lookup("routed_combine")
+    assert loom.launch_config_invoke(tok, [256, 8, 1024])["workgroups"] == (256, 4, 1)
+    assert loom.launch_config_invoke(tok, [1, 32, 260])["workgroups"] == (1, 2, 1)

@@ -423,3 +423,48 @@ def test_sum_guarded_rows_poisoned(loom, device):
         p[:, :, columns:] = np.nan
         g = _np(loom.sum_guarded_rows(torch.from_numpy(p).to(device), count, columns, active))
         assert np.array_equal(g.view(np.uint32), oracle.sum_guarded_rows(v, count, columns, active).view(np.uint32))
+
+
+# ------------------------------------------------------------------ routed row combine
+
+def _run_routed(loom, device, ids, weights, payload):
+    return _np(loom.routed_combine(ids.to(device), weights.to(device), payload.to(device)))
+
+
+@pytest.mark.parametrize("tokens,routes", [(1, 8), (16, 8), (256, 8), (1, 32), (16, 32), (256, 32)])
+def test_routed_combine_page_shapes_bitwise(loom, device, tokens, routes):
+    # the pages' n8/n32 x t1/t16/t256 workloads, 1024-wide rows, 5% missing routes
+    ids, weights, payload = synth.routed_inputs(seed=80 + tokens + routes, tokens=tokens, routes=routes)
+    g = _run_routed(loom, device, ids, weights, payload)
+    ref = oracle.routed_combine(ids.numpy(), weights.numpy(), payload.numpy())[0]
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("tokens,routes,hidden,missing", [(3, 0, 64, 5), (5, 100, 260, 20), (2, 64, 4, 50),
+                                                          (9, 65, 512, 5), (4, 7, 1024, 100), (1, 130, 8, 0)])
+def test_routed_combine_edges_bitwise(loom, device, tokens, routes, hidden, missing):
+    ids, weights, payload = synth.routed_inputs(seed=90 + routes, tokens=tokens, routes=max(routes, 1),
+                                                hidden=hidden, missing_percent=missing)
+    ids, weights = ids[:, :routes].contiguous(), weights[:, :routes].contiguous()
+    w = weights.clone()
+    w[(ids < 0) | (ids >= payload.shape[0])] = float("nan")   # weights of missing routes are never read
+    g = _run_routed(loom, device, ids, w, payload)
+    ref = oracle.routed_combine(ids.numpy(), weights.numpy(), payload.numpy())[0]
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
+def test_routed_combine_no_rows(loom, device):
+    ids = torch.tensor([[0, 1, -1]], dtype=torch.int32)
+    g = _run_routed(loom, device, ids, torch.ones(1, 3), torch.zeros(0, 16))
+    assert np.all(g == 0) and not np.any(np.signbit(g))
+
+
+def test_routed_combine_large_sampled(loom, device):
+    tokens, routes, hidden = 16384, 8, 1024
+    ids, weights, payload = synth.routed_inputs(tokens=tokens, routes=routes, hidden=hidden, device=device)
+    g = _np(loom.routed_combine(ids, weights, payload))
+    rng = np.random.default_rng(11)
+    sample = np.unique(np.concatenate([[0, tokens - 1], rng.integers(0, tokens, 64)]))
+    hp = payload.cpu().numpy()
+    ref = oracle.routed_combine(ids.cpu().numpy()[sample], weights.cpu().numpy()[sample], hp)[0]
+    assert np.array_equal(g[sample].view(np.uint32), ref.view(np.uint32))
