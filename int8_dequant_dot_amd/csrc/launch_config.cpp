@@ -90,10 +90,10 @@ int geo_sum_guarded_rows(const int64_t *w, loom_launch_config *c) {
     return set(c, 1, 32, 0);
 }
 
-// routed_combine(tokens, routes, hidden): one wave per token and 256-column block.
+// routed_combine(tokens, routes, hidden): one wave per token and column block.
 int geo_routed_combine(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 0) return LOOM_ERR_RANGE;
-    return set2(c, w[0], ceil_div(w[2], 256), kSubgroupSize, 0);
+    return set2(c, w[0], ceil_div(w[2], kRoutedColumnsPerWave), kSubgroupSize, 0);
 }
 
 struct Export {

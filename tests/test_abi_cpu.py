@@ -256,5 +256,6 @@ def test_routed_combine_validation(loom, lib):
     assert f(FAKE, FAKE, FAKE + 4, 10, 4, 8, 64, FAKE, None) == loom.ERR_ALIGN
     assert f(FAKE, FAKE, FAKE, 10, 4, 8, 64, FAKE + 8, None) == loom.ERR_ALIGN
     tok = loom.launch_config_lookup("routed_combine")
-    assert loom.launch_config_invoke(tok, [256, 8, 1024])["workgroups"] == (256, 4, 1)
-    assert loom.launch_config_invoke(tok, [1, 32, 260])["workgroups"] == (1, 2, 1)
+    assert loom.launch_config_invoke(tok, [256, 8, 1024])["workgroups"] == (256, 1, 1)  # 1024 columns per wave
+    assert loom.launch_config_invoke(tok, [256, 8, 4096])["workgroups"] == (256, 4, 1)
+    assert loom.launch_config_invoke(tok, [1, 32, 1028])["workgroups"] == (1, 2, 1)

@@ -441,7 +441,8 @@ def test_routed_combine_page_shapes_bitwise(loom, device, tokens, routes):
 
 
 @pytest.mark.parametrize("tokens,routes,hidden,missing", [(3, 0, 64, 5), (5, 100, 260, 20), (2, 64, 4, 50),
-                                                          (9, 65, 512, 5), (4, 7, 1024, 100), (1, 130, 8, 0)])
+                                                          (9, 65, 512, 5), (4, 7, 1024, 100), (1, 130, 8, 0),
+                                                          (3, 9, 2052, 10)])
 def test_routed_combine_edges_bitwise(loom, device, tokens, routes, hidden, missing):
     ids, weights, payload = synth.routed_inputs(seed=90 + routes, tokens=tokens, routes=max(routes, 1),
                                                 hidden=hidden, missing_percent=missing)
