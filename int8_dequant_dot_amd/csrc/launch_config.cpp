@@ -52,10 +52,11 @@ int geo_row_sum_tiles(const int64_t *w, loom_launch_config *c) {
     return set(c, 1, kSubgroupSize, 0);
 }
 
-// row_sums(rows, cols): one wave per tile of 8 rows (the last one the tail).
+// row_sums(rows, cols): one wave per block of TILES_PER_WAVE tiles of 8 rows
+// (the last tile the tail).
 int geo_row_sums(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
-    return set(c, ceil_div(w[0], kTileRows), kSubgroupSize, 0);
+    return set(c, ceil_div(w[0], int64_t(kTileRows) * kRowSumsTilesPerWave), kSubgroupSize, 0);
 }
 
 // segment_sums(segments, cols): one wave per segment.

@@ -52,9 +52,10 @@ __global__ __launch_bounds__(kWave) void row_sum_tiles_kernel(const float *__res
 }
 
 // ----------------------------------------------------------------------------
-// Streaming row sums.  One wave owns one tile of 8 rows (the last tile holds
-// the rows mod 8 tail, so it is the separate guarded tile of TUNE §Derive
-// full tiles).  The tile is walked as one stream of records -- a record is
+// Streaming row sums.  One wave owns kRowSumsTilesPerWave consecutive tiles
+// of 8 rows (the last tile of the matrix holds the rows mod 8 tail, so it is
+// the separate guarded tile of TUNE §Derive full tiles).  The wave's rows are
+// walked as one stream of records -- a record is
 // 64 lanes x VEC contiguous floats of one row (1 KiB for VEC = 4) -- so the
 // read-ahead crosses row boundaries without draining.  Each lane folds its
 // floats into a private partial; at the end of a row the wave64 reduction
@@ -77,8 +78,8 @@ __global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict
     typedef typename vec_of<VEC>::type V;
     constexpr int kBlock = kWave * VEC;  // columns per record
     const int lane = lane_id();
-    const int row0 = blockIdx.x * kTileRows;
-    const int nrows = min(kTileRows, rows - row0);
+    const int row0 = blockIdx.x * (kTileRows * kRowSumsTilesPerWave);
+    const int nrows = min(kTileRows * kRowSumsTilesPerWave, rows - row0);
     const int records_per_row = (cols + kBlock - 1) / kBlock;
 
     // Producer cursor (wave-uniform, kept in SGPRs): the current row and the

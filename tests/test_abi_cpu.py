@@ -85,8 +85,8 @@ def test_launch_config_matches_oracle_geometry(loom):
 
 def test_launch_config_tiles(loom):
     rs = loom.launch_config_lookup("row_sums")
-    for rows in (0, 1, 7, 8, 9, 65536, 65537):
-        assert loom.launch_config_invoke(rs, [rows, 4096])["workgroups"][0] == -(-rows // 8)
+    for rows in (0, 1, 7, 8, 9, 63, 64, 65, 65536, 65537):  # one wave per 8 tiles of 8 rows
+        assert loom.launch_config_invoke(rs, [rows, 4096])["workgroups"][0] == -(-rows // 64)
     seg = loom.launch_config_lookup("segment_sums")
     assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"][0] == 16384
     i8 = loom.launch_config_lookup("i8_dequant_dot")
