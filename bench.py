@@ -12,7 +12,12 @@ Prints one JSON line.  `value` is total algorithmic bytes per step / time per
 step, timed over K back-to-back steps (phase A).  `roofline` is for the
 dominant kernel (row_sums): its algorithmic bytes / its mean duration over K
 back-to-back launches between two HIP events on the launch stream (phase B).  `cpu_baseline` is
-the CPU oracle on the same workload (also used to check the outputs).
+the CPU oracle on the same workload on one core (also used to check the outputs);
+`cpu_baseline_all_cores` runs the same oracle calls over row blocks on every
+usable host core.  `parts` gives each kernel's mean, median and minimum time; the
+pages' own launch-bound shapes (the 63x32 tile, the 1009-element copy, the
+guarded 63x32x4 rows, the 2048x128 packed dot, the 256-token routed combines)
+add `us_graph`, the device time per call inside a HIP graph of back-to-back calls.
 
   python bench.py [--steps K] [--warmup W] [--segments] [--calibrate-copy MiB]
 """
@@ -29,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_OPS = 5.0e15  # dense int8 MFMA, MI355X
 METRIC = "achieved HBM GB/s (and % of peak) for row-sum and int8 dequant-dot"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_sums_65536x4096.json")
 KERNEL_SOURCES = ("device_common.hpp", "internal.hpp", "row_sums.hip")
@@ -40,6 +46,48 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "int8_dequant_dot_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
+
+
+def graph_us(fn, reps: int):
+    """Device time of one call of `fn` (a launch-bound entry point), as
+    (microseconds per call in a HIP graph of `reps` back-to-back calls,
+    microseconds per eagerly issued call).  Between replays the outputs are
+    poisoned by eager fills, and after each replay they must equal those of an
+    eager call bit for bit."""
+    import torch
+    ref = [_bits(t).clone() for t in fn()]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) * 1e3 / reps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            res = fn()
+    times = []
+    for _ in range(5):
+        for t in res:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / reps)
+        for t, r in zip(res, ref):
+            if not torch.equal(_bits(t), r):
+                raise RuntimeError("a graph replay gave a result that differs from the eager call")
+    del g
+    return sorted(times)[len(times) // 2], eager
 
 
 def parse():
@@ -147,7 +195,7 @@ def main():
     # Phase B: each kernel alone, K launches back to back (its input ring
     # still rotating) between two events on the launch stream: its mean
     # duration, with the event overhead amortised over K launches.
-    per_kernel_ms = []
+    per_kernel_ms, per_launch_ms = [], []
     for _, _, fn in kernels:
         fn(0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -158,12 +206,26 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         per_kernel_ms.append(e0.elapsed_time(e1) / K)
+        # the same K launches with an event between each pair, for median and min
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        ev[0].record(stream)
+        for i in range(K):
+            fn(i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_launch_ms.append(sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(K)))
 
     parts = {}
-    for (name, nbytes, _), ms in zip(kernels, per_kernel_ms):
+    for (name, nbytes, _), ms, each in zip(kernels, per_kernel_ms, per_launch_ms):
         gbs = nbytes / (ms * 1e-3) / 1e9
         parts[name] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                       "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+                       "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                       "us_median": round(each[len(each) // 2] * 1e3, 2), "us_min": round(each[0] * 1e3, 2)}
+    # useful int8 operations of the batched product (2 per multiply-add) against
+    # the dense int8 MFMA peak: the product is HBM-bound by a wide margin
+    ops5 = 2 * R5 * K5 * B5
+    parts["i8_dequant_dot_batched"]["TOP/s"] = round(ops5 / (per_kernel_ms[2] * 1e-3) / 1e12, 1)
+    parts["i8_dequant_dot_batched"]["mfma_util"] = round(ops5 / (per_kernel_ms[2] * 1e-3) / INT8_PEAK_OPS, 4)
 
     if args.segments:
         S, CS = 16384, 256
@@ -230,6 +292,34 @@ def main():
                         "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del rid, rw, rp, rout
 
+    # The pages' own shapes are launch-bound: a host call costs more than the
+    # kernel.  Their device time per call comes from a HIP graph of back-to-back
+    # calls; each replay is checked bit for bit against an eager call.
+    tv, tc = synth.tile_inputs(device=dev)
+    cin = synth.copy_inputs(device=dev)
+    cout = torch.empty_like(cin)
+    gv = synth.normal(1, synth.S_VALUES, 0, 63 * 32 * 4, dev).view(63, 32, 4)
+    gout = torch.empty(32, device=dev)
+    pf, ps, pr, pi = synth.packed_dot_inputs(records=128, outputs=2048, device=dev)
+    pout = torch.empty(2048, device=dev)
+    small = {
+        "row_sum_tiles_63x32": (lambda: loom.row_sum_tiles(tv, tc), 63 * 32 * 4 + 32 * 4 + 8),
+        "copy_f32_1009": (lambda: (loom.copy_f32(cin, out=cout),), 1009 * 8),
+        "sum_guarded_rows_63x32x4": (lambda: (loom.sum_guarded_rows(gv, 63, 4, 32, out=gout),), 63 * 32 * 16 + 32 * 4),
+        "packed_dot_2048x128": (lambda: (loom.packed_dot(pf, ps, pr, 128, pi, out=pout),), None),
+    }
+    for tokens, routes in ((256, 8), (256, 32)):
+        rid, rw, rp = synth.routed_inputs(tokens=tokens, routes=routes, hidden=1024, device=dev)
+        rout = torch.empty(tokens, 1024, device=dev)
+        small[f"routed_combine_n{routes}_t{tokens}"] = (
+            (lambda rid=rid, rw=rw, rp=rp, rout=rout: (loom.routed_combine(rid, rw, rp, out=rout),)), None)
+    for label, (fn, nbytes) in small.items():
+        us_graph, us_eager = graph_us(fn, max(K, 64))
+        part = parts.setdefault(label, {"bytes": nbytes, "us": round(us_eager, 2)})
+        part["us_graph"] = round(us_graph, 2)
+        part["GB/s_graph"] = round(part["bytes"] / (us_graph * 1e-6) / 1e9, 1)
+    del pf, ps, pr, pi
+
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- roofline of the dominant kernel
@@ -246,6 +336,7 @@ def main():
 
     # ---------------------------------------------------------------- CPU oracle baseline (+ output check)
     cpu = None
+    cpu_all = None
     check = None
     if not args.no_cpu:
         import oracle
@@ -273,6 +364,42 @@ def main():
                "sample": f"the full step (all three kernels' inputs and outputs), {passes} pass(es), "
                          f"{t_cpu:.1f}s, single-threaded C oracle"}
 
+        # The same oracle calls over disjoint row blocks on every host core
+        # this process may use (at most 16); ctypes drops the GIL for each
+        # call, and each output's arithmetic is unchanged, so the results
+        # must equal the single-threaded ones bit for bit.
+        from concurrent.futures import ThreadPoolExecutor
+        ncores = min(len(os.sched_getaffinity(0)), 16)
+
+        def blocks(n):
+            b = -(-n // ncores)
+            return [(i, min(n, i + b)) for i in range(0, n, b)]
+
+        def threaded_pass(pool):
+            f2 = [pool.submit(oracle.row_sums, hx2[a:b], False) for a, b in blocks(hx2.shape[0])]
+            f4 = [pool.submit(oracle.i8_dequant_dot, hw4[a:b], hs4[a:b], hx4) for a, b in blocks(hw4.shape[0])]
+            f5 = [pool.submit(oracle.i8_dequant_dot, hw5[a:b], hs5[a:b], hx5, hsx5) for a, b in blocks(hw5.shape[0])]
+            return (np.concatenate([f.result()[0] for f in f2]), np.concatenate([f.result()[0] for f in f4]),
+                    np.concatenate([f.result()[0] for f in f5]))
+
+        with ThreadPoolExecutor(ncores) as pool:
+            tpasses, t_all = 0, 0.0
+            while tpasses == 0 or t_all < 5.0:
+                t = time.perf_counter()
+                m2, m4, m5 = threaded_pass(pool)
+                t_all += time.perf_counter() - t
+                if tpasses == 0:
+                    same = all(np.array_equal(u.view(np.uint32), v.view(np.uint32))
+                               for u, v in ((m2, r2), (m4, r4), (m5, r5)))
+                    if not same:
+                        raise RuntimeError("threaded oracle differs from the single-threaded oracle")
+                tpasses += 1
+        cpu_all = {"value": round(tpasses * step_bytes / t_all / 1e9, 3), "unit": "GB/s", "cores": ncores,
+                   "kind": "oracle",
+                   "sample": f"the full step split into {ncores} row blocks per kernel, {tpasses} pass(es), "
+                             f"{t_all:.1f}s; bitwise equal to the single-threaded run"}
+        log(f"oracle on {ncores} cores: {cpu_all}")
+
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -290,6 +417,7 @@ def main():
                    "bytes_per_step": step_bytes, "frac_of_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
         "parts": parts,
         "oracle_check": check,
     }
