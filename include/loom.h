@@ -195,11 +195,8 @@ int loom_i8_dequant_dot(const int32_t *w, const float *w_scale, const int32_t *x
  * each product and sum a separate f32 rounding (no fused multiply-add), so  *
  * the result is the serial recurrence bit for bit.                          *
  *   fields  : int32[records][outputs], record-major (consecutive outputs    *
- *             contiguous), 4-byte aligned (16-byte when outputs >= 65536,   *
- *             outputs % 4 == 0 and streams % 4 == 0: then each lane takes   *
- *             four outputs with 128-bit loads)                              *
+ *             contiguous), 4-byte aligned                                   *
  *   scales  : binary16 bit patterns [records][outputs], 2-byte aligned      *
- *             (8-byte in the four-outputs case)                             *
  *   rhs     : f32[records][streams][4] activations, 16-byte aligned; the    *
  *             streams are shared by all outputs (output o reads o mod       *
  *             streams)                                                      *

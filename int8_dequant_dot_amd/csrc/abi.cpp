@@ -123,8 +123,6 @@ extern "C" int loom_packed_dot(const int32_t *fields, const uint16_t *scales, co
     if (misaligned(fields, 4) || misaligned(scales, 2) || misaligned(rhs, 16) || misaligned(initial, 4) ||
         misaligned(out, 4))
         return LOOM_ERR_ALIGN;
-    if (loom::packed_dot_outputs_per_lane(outputs, streams) == 4 && (misaligned(fields, 16) || misaligned(scales, 8)))
-        return LOOM_ERR_ALIGN;
     loom_launch_config cfg;
     const int64_t w[3] = {outputs, count, streams};
     if (int st = loom::evaluate_launch(loom::kPackedDot, w, &cfg)) return st;

@@ -84,7 +84,7 @@ struct GemvRecord {
 };
 
 template <bool FULL, bool VEC16, int DEPTH>
-__global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
+__global__ __launch_bounds__(kWave * kGemvWaves) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
                                                         const int32_t *__restrict__ x,
                                                         const float *__restrict__ x_scale, int rows, int kw,
                                                         float *__restrict__ out, int32_t *__restrict__ acc_out) {
@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
     constexpr int TR = kGemvTileRows;
     static_assert(TR * kGemvTilesPerWave <= kWave, "one lane per row of the wave's block");
     const int lane = lane_id();
-    const int row0 = blockIdx.x * (TR * kGemvTilesPerWave);
+    const int row0 = (blockIdx.x * kGemvWaves + (int)(threadIdx.x / kWave)) * (TR * kGemvTilesPerWave);
+    if (row0 >= rows) return;  // a surplus wave of the last workgroup
     const int wave_rows = min(TR * kGemvTilesPerWave, rows - row0);
     const int tiles = (wave_rows + TR - 1) / TR;
     const int records_per_tile = (kw + kBlockWords - 1) / kBlockWords;

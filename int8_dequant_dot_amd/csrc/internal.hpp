@@ -46,6 +46,9 @@ static_assert(kTileRows * kRowSumsTilesPerWave <= 64, "one lane per row of a wav
 #ifndef LOOM_GEMV_TILES_PER_WAVE
 #define LOOM_GEMV_TILES_PER_WAVE 1
 #endif
+#ifndef LOOM_GEMV_WAVES
+#define LOOM_GEMV_WAVES 1     // waves per GEMV workgroup, each with its own tiles
+#endif
 #ifndef LOOM_MFMA_KSPLIT
 #define LOOM_MFMA_KSPLIT 4    // 4 waves per 16-row tile: 7168 waves for 28672 rows
 #endif
@@ -54,19 +57,25 @@ static_assert(kTileRows * kRowSumsTilesPerWave <= 64, "one lane per row of a wav
 #endif
 constexpr int kGemvTileRows = LOOM_GEMV_TILE_ROWS;
 constexpr int kGemvTilesPerWave = LOOM_GEMV_TILES_PER_WAVE;
+constexpr int kGemvWaves = LOOM_GEMV_WAVES;
 constexpr int kMfmaTileRows = 16;
 constexpr int kMfmaKSplit = LOOM_MFMA_KSPLIT;
 constexpr bool kMfmaStage = LOOM_MFMA_STAGE != 0;
 constexpr uint32_t kMfmaStageBytes = 16 * 256;  // per wave: 16 rows x 256 B
-// Outputs per lane of the packed-dot recurrence: 4 once there are enough
-// outputs to fill the GPU with wide loads and the stream count keeps four
-// consecutive outputs on four consecutive streams; otherwise 1 (the pages'
-// one lane per output, best for the latency-bound small shapes).
+// Outputs per lane of the packed-dot recurrence: kPackedDotWide, spaced one
+// wave apart, once there are enough outputs to fill the GPU and the stream
+// count divides the wave width (every output of a lane then reads the same
+// stream); otherwise 1 (the pages' one lane per output, best for the
+// latency-bound small shapes).
 #ifndef LOOM_PACKED_DOT_WIDE_MIN
 #define LOOM_PACKED_DOT_WIDE_MIN 65536
 #endif
+#ifndef LOOM_PACKED_DOT_WIDE
+#define LOOM_PACKED_DOT_WIDE 4
+#endif
+constexpr int kPackedDotWide = LOOM_PACKED_DOT_WIDE;
 constexpr int packed_dot_outputs_per_lane(int64_t outputs, int64_t streams) {
-    return (outputs >= LOOM_PACKED_DOT_WIDE_MIN && outputs % 4 == 0 && streams % 4 == 0) ? 4 : 1;
+    return (outputs >= LOOM_PACKED_DOT_WIDE_MIN && 64 % streams == 0) ? kPackedDotWide : 1;
 }
 
 // Columns of the routed combine per wave (a multiple of 256: 1 KiB slices of

@@ -72,14 +72,16 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
     if (w[2] == 1)
-        return set(c, ceil_div(w[0], int64_t(kGemvTileRows) * kGemvTilesPerWave), kSubgroupSize, 0);
+        return set(c, ceil_div(w[0], int64_t(kGemvTileRows) * kGemvTilesPerWave * kGemvWaves),
+                   kSubgroupSize * kGemvWaves, 0);
     return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * kMfmaKSplit,
                (kMfmaKSplit - 1) * mfma_col_tiles(w[2]) * 4 * kSubgroupSize * 4 +
                    (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));
 }
 
 // packed_dot(outputs, count, streams): 256 lanes per workgroup, one output
-// per lane, or four for large output counts (see packed_dot_outputs_per_lane).
+// per lane, or several for large output counts (see
+// packed_dot_outputs_per_lane).
 int geo_packed_dot(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
     return set(c, ceil_div(w[0], 256 * packed_dot_outputs_per_lane(w[0], w[2])), 256, 0);

@@ -15,21 +15,15 @@ namespace loom {
 #define LOOM_PACKED_DOT_DEPTH 8  // records in flight per lane: the pages' shape is latency-bound
 #endif
 #ifndef LOOM_PACKED_DOT_DEPTH_WIDE
-#define LOOM_PACKED_DOT_DEPTH_WIDE 4  // 4 outputs per lane: 88 B per record
+#define LOOM_PACKED_DOT_DEPTH_WIDE 6  // several outputs per lane
 #endif
 constexpr int kPackedDotDepth = LOOM_PACKED_DOT_DEPTH;
 constexpr int kPackedDotDepthWide = LOOM_PACKED_DOT_DEPTH_WIDE;
 
-template <int OPL> struct PackedRecord;
-template <> struct PackedRecord<1> {
+struct PackedRecord {
     int32_t word;       // four signed bytes, element j in byte j
     uint16_t scale;     // binary16 bits
     float4v act;        // the output's activation stream for this record
-};
-template <> struct PackedRecord<4> {
-    int4v word;         // 4 consecutive outputs
-    uint2v scale;       // their 4 binary16 scales
-    float4v act[4];     // their 4 consecutive activation streams
 };
 
 // One record of one output: each of the four products is added to the
@@ -44,72 +38,105 @@ __device__ __forceinline__ float packed_step(float sum, int32_t word, uint16_t s
     return sum;
 }
 
-// Each lane owns OPL consecutive outputs (the page: one, the output index is
-// the lane of its [record][output] views).  Records are walked in order
-// through the read-ahead ring; fields and scales are read once
-// (non-temporal), the activation streams are shared by every output and stay
-// cached.  OPL = 4 needs outputs and streams divisible by 4 (consecutive
-// outputs then read consecutive streams) and 16-byte aligned rows.
-template <int DEPTH, int OPL>
+// One output per lane (the page's mapping: the output index is the lane of
+// its [record][output] views).  Records are walked in order through the
+// read-ahead ring; fields and scales are read once (non-temporal), the
+// activation streams are shared by every output and stay cached.
+template <int DEPTH>
 __global__ __launch_bounds__(256) void packed_dot_kernel(const int32_t *__restrict__ fields,
                                                          const uint16_t *__restrict__ scales,
                                                          const float *__restrict__ rhs, int streams,
                                                          const float *__restrict__ initial, int count,
                                                          int64_t outputs, float *__restrict__ out) {
-    const int64_t o = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * OPL;
+    const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (o >= outputs) return;
-    float sum[OPL];
-#pragma unroll
-    for (int i = 0; i < OPL; ++i) sum[i] = initial ? initial[o + i] : 0.0f;
+    float sum = initial ? initial[o] : 0.0f;
     const int32_t *fp = fields + o;
     const uint16_t *sp = scales + o;
     const float4v *ap = reinterpret_cast<const float4v *>(rhs) + o % streams;
-    pipelined<DEPTH, PackedRecord<OPL>>(
+    pipelined<DEPTH, PackedRecord>(
         count,
         [&]() {
-            PackedRecord<OPL> q;
-            if constexpr (OPL == 1) {
-                q.word = load_stream(fp);
-                q.scale = load_stream(sp);
-                q.act = *ap;
-            } else {
-                q.word = load_stream(reinterpret_cast<const int4v *>(fp));
-                q.scale = load_stream(reinterpret_cast<const uint2v *>(sp));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) q.act[i] = ap[i];
-            }
+            PackedRecord q;
+            q.word = load_stream(fp);
+            q.scale = load_stream(sp);
+            q.act = *ap;
             fp += outputs;
             sp += outputs;
             ap += streams;
             return q;
         },
-        [&](const PackedRecord<OPL> &q) {
-            if constexpr (OPL == 1) {
-                sum[0] = packed_step(sum[0], q.word, q.scale, q.act);
-            } else {
-                sum[0] = packed_step(sum[0], q.word.x, (uint16_t)(q.scale.x & 0xFFFF), q.act[0]);
-                sum[1] = packed_step(sum[1], q.word.y, (uint16_t)(q.scale.x >> 16), q.act[1]);
-                sum[2] = packed_step(sum[2], q.word.z, (uint16_t)(q.scale.y & 0xFFFF), q.act[2]);
-                sum[3] = packed_step(sum[3], q.word.w, (uint16_t)(q.scale.y >> 16), q.act[3]);
+        [&](const PackedRecord &q) { sum = packed_step(sum, q.word, q.scale, q.act); });
+    out[o] = sum;
+}
+
+// Wide form with OPL outputs per lane spaced one wave apart: lane l of a wave
+// whose block starts at output `base` (a multiple of 64 * OPL) owns outputs
+// base + l + 64 j, j < OPL.  When the stream count divides 64, every one of
+// them reads stream l mod streams, so a record needs a single 16-byte
+// activation load per lane (one contiguous 1 KiB per wave), while each
+// output's field word and scale still come from fully coalesced rows.
+// Outputs past the end are clamped to the last one for loading and never
+// stored.
+template <int OPL> struct SpacedRecord {
+    int32_t word[OPL];
+    uint16_t scale[OPL];
+    float4v act;
+};
+
+template <int DEPTH, int OPL>
+__global__ __launch_bounds__(256) void packed_dot_spaced_kernel(const int32_t *__restrict__ fields,
+                                                                const uint16_t *__restrict__ scales,
+                                                                const float *__restrict__ rhs, int streams,
+                                                                const float *__restrict__ initial, int count,
+                                                                int64_t outputs, float *__restrict__ out) {
+    const int lane = lane_id();
+    const int64_t base = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * (kWave * OPL);
+    if (base >= outputs) return;
+    int64_t o[OPL];
+    float sum[OPL];
+#pragma unroll
+    for (int j = 0; j < OPL; ++j) {
+        o[j] = min(base + lane + kWave * j, outputs - 1);
+        sum[j] = initial ? initial[o[j]] : 0.0f;
+    }
+    const int32_t *fp = fields;
+    const uint16_t *sp = scales;
+    const float4v *ap = reinterpret_cast<const float4v *>(rhs) + lane % streams;
+    pipelined<DEPTH, SpacedRecord<OPL>>(
+        count,
+        [&]() {
+            SpacedRecord<OPL> q;
+#pragma unroll
+            for (int j = 0; j < OPL; ++j) {
+                q.word[j] = load_stream(fp + o[j]);
+                q.scale[j] = load_stream(sp + o[j]);
             }
+            q.act = *ap;
+            fp += outputs;
+            sp += outputs;
+            ap += streams;
+            return q;
+        },
+        [&](const SpacedRecord<OPL> &q) {
+#pragma unroll
+            for (int j = 0; j < OPL; ++j) sum[j] = packed_step(sum[j], q.word[j], q.scale[j], q.act);
         });
 #pragma unroll
-    for (int i = 0; i < OPL; ++i) out[o + i] = sum[i];
+    for (int j = 0; j < OPL; ++j)
+        if (base + lane + kWave * j < outputs) out[base + lane + kWave * j] = sum[j];
 }
 
 hipError_t launch_packed_dot(const loom_launch_config &cfg, const int32_t *fields, const uint16_t *scales,
                              const float *rhs, int streams, const float *initial, int count, int64_t outputs,
                              float *out, hipStream_t stream) {
     const dim3 grid(cfg.workgroups[0]), block(cfg.workgroup_size[0]);
-    if (packed_dot_outputs_per_lane(outputs, streams) == 4) {
-        const bool aligned = reinterpret_cast<uintptr_t>(fields) % 16 == 0 && reinterpret_cast<uintptr_t>(scales) % 8 == 0;
-        if (!aligned) return hipErrorInvalidValue;  // the entry point checks this first
-        packed_dot_kernel<kPackedDotDepthWide, 4><<<grid, block, 0, stream>>>(fields, scales, rhs, streams, initial,
-                                                                               count, outputs, out);
-    } else {
-        packed_dot_kernel<kPackedDotDepth, 1><<<grid, block, 0, stream>>>(fields, scales, rhs, streams, initial,
-                                                                           count, outputs, out);
-    }
+    if (packed_dot_outputs_per_lane(outputs, streams) > 1)
+        packed_dot_spaced_kernel<kPackedDotDepthWide, kPackedDotWide><<<grid, block, 0, stream>>>(
+            fields, scales, rhs, streams, initial, count, outputs, out);
+    else
+        packed_dot_kernel<kPackedDotDepth><<<grid, block, 0, stream>>>(fields, scales, rhs, streams, initial, count,
+                                                                       outputs, out);
     return hipGetLastError();
 }
 

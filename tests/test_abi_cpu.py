@@ -224,7 +224,8 @@ def test_packed_dot_validation(loom, lib):
     tok = loom.launch_config_lookup("packed_dot")
     assert loom.launch_config_invoke(tok, [2048, 128, 64])["workgroups"] == (8, 1, 1)
     assert loom.launch_config_invoke(tok, [262144, 128, 64])["workgroups"] == (256, 1, 1)  # 4 outputs per lane
-    assert loom.launch_config_invoke(tok, [262146, 128, 64])["workgroups"] == (1025, 1, 1)
+    assert loom.launch_config_invoke(tok, [262146, 128, 16])["workgroups"] == (257, 1, 1)
+    assert loom.launch_config_invoke(tok, [262144, 128, 128])["workgroups"] == (1024, 1, 1)  # 128 streams: one
     assert loom.launch_config_invoke(tok, [2049, 0, 3])["workgroups"] == (9, 1, 1)
 
 

@@ -367,7 +367,11 @@ def test_packed_dot_page_shape_bitwise(loom, device, count):
 
 
 @pytest.mark.parametrize("outputs,streams,count", [(1, 1, 5), (100, 3, 17), (70001, 64, 9), (300, 100, 33),
-                                                   (64, 64, 128)])
+                                                   (64, 64, 128),
+                                                   # several outputs per lane, a ragged last wave
+                                                   (65536 + 37, 1, 6), (65536 + 1000, 16, 11), (66560, 32, 21),
+                                                   # 128 streams do not divide the wave: one output per lane
+                                                   (65536, 128, 7)])
 def test_packed_dot_odd_shapes_bitwise(loom, device, outputs, streams, count):
     fields, scales, rhs, initial = synth.packed_dot_inputs(seed=70 + outputs, records=max(count, 1) + 2,
                                                           outputs=outputs, streams=streams)
