@@ -12,9 +12,6 @@ namespace loom {
 #ifndef LOOM_ROUTED_DEPTH
 #define LOOM_ROUTED_DEPTH 6   // payload rows in flight per wave
 #endif
-#ifndef LOOM_ROUTED_NT_STORE
-#define LOOM_ROUTED_NT_STORE 0
-#endif
 constexpr int kRoutedDepth = LOOM_ROUTED_DEPTH;
 constexpr int kRoutedVecs = kRoutedColumnsPerWave / (kWave * 4);  // float4s per lane per route
 
@@ -100,14 +97,7 @@ __global__ __launch_bounds__(kWave) void routed_combine_kernel(const int32_t *__
     }
 #pragma unroll
     for (int v = 0; v < VECS; ++v)
-        if (c + v * kWave * 4 < hidden) {
-            float4v *dst = reinterpret_cast<float4v *>(out + t * hidden + c + v * kWave * 4);
-#if LOOM_ROUTED_NT_STORE
-            __builtin_nontemporal_store(acc[v], dst);
-#else
-            *dst = acc[v];
-#endif
-        }
+        if (c + v * kWave * 4 < hidden) *reinterpret_cast<float4v *>(out + t * hidden + c + v * kWave * 4) = acc[v];
 }
 
 hipError_t launch_routed_combine(const loom_launch_config &cfg, const int32_t *ids, const float *weights,
