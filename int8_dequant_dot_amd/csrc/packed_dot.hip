@@ -84,35 +84,39 @@ template <int OPL> struct SpacedRecord {
     float4v act;
 };
 
-template <int DEPTH, int OPL>
-__global__ __launch_bounds__(256) void packed_dot_spaced_kernel(const int32_t *__restrict__ fields,
-                                                                const uint16_t *__restrict__ scales,
-                                                                const float *__restrict__ rhs, int streams,
-                                                                const float *__restrict__ initial, int count,
-                                                                int64_t outputs, float *__restrict__ out) {
+// The work of one wave.  FULL: all 64 * OPL outputs exist, so every load
+// address is a wave-uniform row pointer (scalar registers) plus the lane's
+// fixed 32-bit offset plus an immediate 256 j / 128 j: no per-record vector
+// address arithmetic.  Otherwise outputs past the end are clamped to the
+// last one for loading and never stored.
+template <int DEPTH, int OPL, bool FULL>
+__device__ __forceinline__ void packed_dot_spaced_wave(const int32_t *__restrict__ fields,
+                                                       const uint16_t *__restrict__ scales,
+                                                       const float *__restrict__ rhs, int streams,
+                                                       const float *__restrict__ initial, int count,
+                                                       int64_t outputs, float *__restrict__ out, int64_t base) {
     const int lane = lane_id();
-    const int64_t base = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * (kWave * OPL);
-    if (base >= outputs) return;
-    int64_t o[OPL];
+    int lo[OPL];  // the lane's outputs, relative to base
     float sum[OPL];
 #pragma unroll
     for (int j = 0; j < OPL; ++j) {
-        o[j] = min(base + lane + kWave * j, outputs - 1);
-        sum[j] = initial ? initial[o[j]] : 0.0f;
+        lo[j] = FULL ? lane + kWave * j : (int)(min(base + lane + kWave * j, outputs - 1) - base);
+        sum[j] = initial ? initial[base + lo[j]] : 0.0f;
     }
-    const int32_t *fp = fields;
-    const uint16_t *sp = scales;
-    const float4v *ap = reinterpret_cast<const float4v *>(rhs) + lane % streams;
+    const int32_t *fp = fields + base;
+    const uint16_t *sp = scales + base;
+    const float4v *ap = reinterpret_cast<const float4v *>(rhs);
+    const int act = lane % streams;
     pipelined<DEPTH, SpacedRecord<OPL>>(
         count,
         [&]() {
             SpacedRecord<OPL> q;
 #pragma unroll
             for (int j = 0; j < OPL; ++j) {
-                q.word[j] = load_stream(fp + o[j]);
-                q.scale[j] = load_stream(sp + o[j]);
+                q.word[j] = load_stream(fp + lo[j]);
+                q.scale[j] = load_stream(sp + lo[j]);
             }
-            q.act = *ap;
+            q.act = ap[act];
             fp += outputs;
             sp += outputs;
             ap += streams;
@@ -124,7 +128,23 @@ __global__ __launch_bounds__(256) void packed_dot_spaced_kernel(const int32_t *_
         });
 #pragma unroll
     for (int j = 0; j < OPL; ++j)
-        if (base + lane + kWave * j < outputs) out[base + lane + kWave * j] = sum[j];
+        if (FULL || base + lane + kWave * j < outputs) out[base + lane + kWave * j] = sum[j];
+}
+
+template <int DEPTH, int OPL>
+__global__ __launch_bounds__(256) void packed_dot_spaced_kernel(const int32_t *__restrict__ fields,
+                                                                const uint16_t *__restrict__ scales,
+                                                                const float *__restrict__ rhs, int streams,
+                                                                const float *__restrict__ initial, int count,
+                                                                int64_t outputs, float *__restrict__ out) {
+    // the wave index within the workgroup is the same in every lane
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int64_t base = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave) * (kWave * OPL);
+    if (base >= outputs) return;
+    if (base + kWave * OPL <= outputs)
+        packed_dot_spaced_wave<DEPTH, OPL, true>(fields, scales, rhs, streams, initial, count, outputs, out, base);
+    else
+        packed_dot_spaced_wave<DEPTH, OPL, false>(fields, scales, rhs, streams, initial, count, outputs, out, base);
 }
 
 hipError_t launch_packed_dot(const loom_launch_config &cfg, const int32_t *fields, const uint16_t *scales,
