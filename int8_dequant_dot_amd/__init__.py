@@ -112,6 +112,9 @@ def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        # the C ABI launches on the current HIP device
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     return t
 
 

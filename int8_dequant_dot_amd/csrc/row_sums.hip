@@ -98,11 +98,13 @@ __global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict
         [&]() {
             const float *bp = rp + lcol;
             V v = V(0.0f);
-            if (FULL || lcol + lane_col < cols) v = load_stream(reinterpret_cast<const V *>(bp + lane_col));
-            lcol += kBlock;
-            if (lcol >= cols) {
+            // (compared as differences, which cannot overflow for any cols < 2^31)
+            if (FULL || lane_col < cols - lcol) v = load_stream(reinterpret_cast<const V *>(bp + lane_col));
+            if (lcol >= cols - kBlock) {
                 lcol = 0;
                 rp += row_stride;
+            } else {
+                lcol += kBlock;
             }
             return v;
         },
