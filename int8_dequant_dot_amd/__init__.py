@@ -122,14 +122,30 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _require(cond: bool, what: str):
+    if not cond:
+        raise ValueError(what)
+
+
+def _buffer(t: torch.Tensor | None, dtype, numel: int, name: str, optional: bool = False):
+    """A caller-supplied input or output buffer: a contiguous device tensor of `dtype` holding at
+    least `numel` elements (the kernels read or write that many from its start)."""
+    if t is None:
+        _require(optional, f"{name} is required")
+        return None
+    _dev(t, dtype, name)
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+    _require(t.numel() >= numel, f"{name} holds {t.numel()} elements, {numel} are needed")
+    return t
+
+
 def copy_f32(inp: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """out[i] = inp[i] for i < inp.numel(); elements of ``out`` beyond that are untouched."""
     _dev(inp, torch.float32, "inp")
-    assert inp.is_contiguous()
+    _require(inp.is_contiguous(), "inp must be contiguous")
     if out is None:
         out = torch.empty_like(inp)
-    _dev(out, torch.float32, "out")
-    assert out.is_contiguous() and out.numel() >= inp.numel()
+    _buffer(out, torch.float32, inp.numel(), "out")
     _check(_lib.loom_copy_f32(_ptr(inp), _ptr(out), inp.numel(), _stream(inp)), "copy_f32")
     return out
 
@@ -137,10 +153,9 @@ def copy_f32(inp: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor
 def row_sum_tiles(values: torch.Tensor, count: int, initial: torch.Tensor | None = None):
     """values [rows_alloc][32] f32 -> (sums[32] f32, final_row int32[1], tail_count int32[1])."""
     _dev(values, torch.float32, "values")
-    assert values.dim() == 2 and values.shape[1] == 32 and values.is_contiguous()
-    if initial is not None:
-        _dev(initial, torch.float32, "initial")
-        assert initial.numel() == 32 and initial.is_contiguous()
+    _require(values.dim() == 2 and values.shape[1] == 32 and values.is_contiguous(),
+             "values must be a contiguous [rows][32] tensor")
+    _buffer(initial, torch.float32, 32, "initial", optional=True)
     sums = torch.empty(32, dtype=torch.float32, device=values.device)
     fr = torch.empty(1, dtype=torch.int32, device=values.device)
     tc = torch.empty(1, dtype=torch.int32, device=values.device)
@@ -152,12 +167,12 @@ def row_sum_tiles(values: torch.Tensor, count: int, initial: torch.Tensor | None
 def row_sums(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """x [rows][cols] f32 with unit column stride (any row stride) -> out [rows]."""
     _dev(x, torch.float32, "x")
-    assert x.dim() == 2 and (x.stride(1) == 1 or x.shape[1] <= 1)
+    _require(x.dim() == 2 and (x.stride(1) == 1 or x.shape[1] <= 1), "x must be [rows][cols] with unit column stride")
     rows, cols = x.shape
     stride = x.stride(0) if rows > 1 else max(cols, 1)
     if out is None:
         out = torch.empty(rows, dtype=torch.float32, device=x.device)
-    _dev(out, torch.float32, "out")
+    _buffer(out, torch.float32, rows, "out")
     _check(_lib.loom_row_sums(_ptr(x), rows, cols, stride, _ptr(out), _stream(x)), "row_sums")
     return out
 
@@ -167,13 +182,17 @@ def segment_sums(x: torch.Tensor, offsets: torch.Tensor, out: torch.Tensor | Non
     """x [total_rows][cols] f32, offsets int64 [S+1] (CSR) -> (out [S][cols], tail_counts int32 [S])."""
     _dev(x, torch.float32, "x")
     _dev(offsets, torch.int64, "offsets")
-    assert x.dim() == 2 and x.is_contiguous() and offsets.dim() == 1 and offsets.is_contiguous()
+    _require(x.dim() == 2 and x.is_contiguous(), "x must be a contiguous [total_rows][cols] tensor")
+    _require(offsets.dim() == 1 and offsets.is_contiguous() and offsets.numel() >= 1,
+             "offsets must be a contiguous [segments + 1] tensor")
     S = offsets.numel() - 1
     cols = x.shape[1]
     if out is None:
         out = torch.empty(S, cols, dtype=torch.float32, device=x.device)
+    _buffer(out, torch.float32, S * cols, "out")
     if tail_counts is None and want_tails:
         tail_counts = torch.empty(S, dtype=torch.int32, device=x.device)
+    _buffer(tail_counts, torch.int32, S, "tail_counts", optional=True)
     _check(_lib.loom_segment_sums(_ptr(x), x.shape[0], _ptr(offsets), S, cols, _ptr(out), _ptr(tail_counts),
                                   _stream(x)), "segment_sums")
     return out, tail_counts
@@ -184,18 +203,21 @@ def i8_dequant_dot(w: torch.Tensor, w_scale: torch.Tensor, x: torch.Tensor, x_sc
     """w int32 [rows][k/4] (packed int8), x int32 [batch][k/4] or [k/4] -> out f32 [rows][batch] (and acc)."""
     _dev(w, torch.int32, "w")
     _dev(x, torch.int32, "x")
-    _dev(w_scale, torch.float32, "w_scale")
     if x.dim() == 1:
         x = x.view(1, -1)
-    assert w.dim() == 2 and w.is_contiguous() and x.is_contiguous() and x.shape[1] == w.shape[1]
+    _require(w.dim() == 2 and w.is_contiguous(), "w must be a contiguous [rows][k/4] tensor")
+    _require(x.dim() == 2 and x.is_contiguous() and x.shape[1] == w.shape[1],
+             "x must be a contiguous [batch][k/4] tensor with the same k as w")
     rows, kw = w.shape
     batch = x.shape[0]
-    if x_scale is not None:
-        _dev(x_scale, torch.float32, "x_scale")
+    _buffer(w_scale, torch.float32, rows, "w_scale")
+    _buffer(x_scale, torch.float32, batch, "x_scale", optional=True)
     if out is None:
         out = torch.empty(rows, batch, dtype=torch.float32, device=w.device)
+    _buffer(out, torch.float32, rows * batch, "out")
     if acc is None and want_acc:
         acc = torch.empty(rows, batch, dtype=torch.int32, device=w.device)
+    _buffer(acc, torch.int32, rows * batch, "acc", optional=True)
     _check(_lib.loom_i8_dequant_dot(_ptr(w), _ptr(w_scale), _ptr(x), _ptr(x_scale), rows, 4 * kw, batch,
                                     _ptr(out), _ptr(acc), _stream(w)), "i8_dequant_dot")
     return (out, acc) if want_acc else out
@@ -210,14 +232,17 @@ def packed_dot(fields: torch.Tensor, scales: torch.Tensor, rhs: torch.Tensor, co
         scales = scales.view(torch.int16)
     if scales.dtype not in (torch.int16, torch.uint16):
         raise TypeError("scales must hold binary16 bit patterns (float16, int16 or uint16)")
+    _dev(scales, scales.dtype, "scales")
     _dev(rhs, torch.float32, "rhs")
-    assert fields.dim() == 2 and fields.is_contiguous() and scales.shape == fields.shape and scales.is_contiguous()
-    assert rhs.dim() == 3 and rhs.shape[2] == 4 and rhs.is_contiguous() and rhs.shape[0] >= count
+    _require(fields.dim() == 2 and fields.is_contiguous(), "fields must be a contiguous [records][outputs] tensor")
+    _require(scales.shape == fields.shape and scales.is_contiguous(), "scales must be contiguous, shaped as fields")
+    _require(rhs.dim() == 3 and rhs.shape[2] == 4 and rhs.is_contiguous() and rhs.shape[0] >= count,
+             "rhs must be a contiguous [records >= count][streams][4] tensor")
     records, outputs = fields.shape
-    if initial is not None:
-        _dev(initial, torch.float32, "initial")
+    _buffer(initial, torch.float32, outputs, "initial", optional=True)
     if out is None:
         out = torch.empty(outputs, dtype=torch.float32, device=fields.device)
+    _buffer(out, torch.float32, outputs, "out")
     _check(_lib.loom_packed_dot(_ptr(fields), _ptr(scales), _ptr(rhs), rhs.shape[1], _ptr(initial), records, count,
                                 outputs, _ptr(out), _stream(fields)), "packed_dot")
     return out
@@ -227,9 +252,11 @@ def sum_guarded_rows(values: torch.Tensor, count: int, columns: int, active_lane
                      out: torch.Tensor | None = None) -> torch.Tensor:
     """values f32 [rows_alloc][32][4] -> sums f32 [32] (the pages' guarded ragged row sum)."""
     _dev(values, torch.float32, "values")
-    assert values.dim() == 3 and tuple(values.shape[1:]) == (32, 4) and values.is_contiguous()
+    _require(values.dim() == 3 and tuple(values.shape[1:]) == (32, 4) and values.is_contiguous(),
+             "values must be a contiguous [rows][32][4] tensor")
     if out is None:
         out = torch.empty(32, dtype=torch.float32, device=values.device)
+    _buffer(out, torch.float32, 32, "out")
     _check(_lib.loom_sum_guarded_rows(_ptr(values), values.shape[0], count, columns, active_lanes, _ptr(out),
                                       _stream(values)), "sum_guarded_rows")
     return out
@@ -242,12 +269,14 @@ def routed_combine(ids: torch.Tensor, weights: torch.Tensor, payload: torch.Tens
     _dev(ids, torch.int32, "ids")
     _dev(weights, torch.float32, "weights")
     _dev(payload, torch.float32, "payload")
-    assert ids.dim() == 2 and ids.is_contiguous() and weights.shape == ids.shape and weights.is_contiguous()
-    assert payload.dim() == 2 and payload.is_contiguous()
+    _require(ids.dim() == 2 and ids.is_contiguous(), "ids must be a contiguous [tokens][routes] tensor")
+    _require(weights.shape == ids.shape and weights.is_contiguous(), "weights must be contiguous, shaped as ids")
+    _require(payload.dim() == 2 and payload.is_contiguous(), "payload must be a contiguous [rows][hidden] tensor")
     tokens, routes = ids.shape
     num_rows, hidden = payload.shape
     if out is None:
         out = torch.empty(tokens, hidden, dtype=torch.float32, device=ids.device)
+    _buffer(out, torch.float32, tokens * hidden, "out")
     _check(_lib.loom_routed_combine(_ptr(ids), _ptr(weights), _ptr(payload), num_rows, tokens, routes, hidden,
                                     _ptr(out), _stream(ids)), "routed_combine")
     return out
@@ -255,7 +284,8 @@ def routed_combine(ids: torch.Tensor, weights: torch.Tensor, payload: torch.Tens
 
 def pack_int8(t: torch.Tensor) -> torch.Tensor:
     """View an int8 [..., k] tensor (k % 4 == 0) as packed int32 [..., k/4] words (no copy)."""
-    assert t.dtype == torch.int8 and t.shape[-1] % 4 == 0 and t.is_contiguous()
+    _require(t.dtype == torch.int8 and t.shape[-1] % 4 == 0 and t.is_contiguous(),
+             "pack_int8 needs a contiguous int8 tensor whose last dimension is a multiple of 4")
     if t.shape[-1] == 0:
         return torch.empty(*t.shape[:-1], 0, dtype=torch.int32, device=t.device)
     return t.view(torch.int32)

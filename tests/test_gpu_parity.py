@@ -473,3 +473,45 @@ def test_routed_combine_large_sampled(loom, device):
     hp = payload.cpu().numpy()
     ref = oracle.routed_combine(ids.cpu().numpy()[sample], weights.cpu().numpy()[sample], hp)[0]
     assert np.array_equal(g[sample].view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ binding checks (nothing is launched)
+
+def test_binding_rejects_short_buffers(loom, device):
+    # the C ABI takes raw pointers; the binding refuses caller buffers that are
+    # too small, of the wrong type or not contiguous, before anything is enqueued
+    x = torch.zeros(8, 256, device=device)
+    with pytest.raises(ValueError):
+        loom.row_sums(x, out=torch.empty(7, device=device))
+    w = torch.zeros(16, 64, dtype=torch.int32, device=device)
+    v = torch.zeros(2, 64, dtype=torch.int32, device=device)
+    with pytest.raises(ValueError):
+        loom.i8_dequant_dot(w, torch.ones(15, device=device), v)
+    with pytest.raises(ValueError):
+        loom.i8_dequant_dot(w, torch.ones(16, device=device), v, torch.ones(1, device=device))
+    with pytest.raises(ValueError):
+        loom.i8_dequant_dot(w, torch.ones(16, device=device), v, out=torch.empty(16, 1, device=device))
+    with pytest.raises(ValueError):
+        loom.i8_dequant_dot(w, torch.ones(16, device=device), v, acc=torch.empty(31, dtype=torch.int32, device=device))
+    with pytest.raises(TypeError):
+        loom.i8_dequant_dot(w, torch.ones(16, device=device), v, out=torch.empty(16, 2, dtype=torch.float16, device=device))
+    off = torch.tensor([0, 3, 8], dtype=torch.int64, device=device)
+    with pytest.raises(ValueError):
+        loom.segment_sums(x, off, out=torch.empty(2, 255, device=device))
+    with pytest.raises(ValueError):
+        loom.segment_sums(x, off, tail_counts=torch.empty(1, dtype=torch.int32, device=device))
+    f = torch.zeros(4, 100, dtype=torch.int32, device=device)
+    s16 = torch.zeros(4, 100, dtype=torch.int16, device=device)
+    r = torch.zeros(4, 64, 4, device=device)
+    with pytest.raises(ValueError):
+        loom.packed_dot(f, s16, r, 4, initial=torch.zeros(99, device=device))
+    with pytest.raises(ValueError):
+        loom.packed_dot(f, s16, r, 4, out=torch.empty(100, 2, device=device).t())
+    ids = torch.zeros(3, 2, dtype=torch.int32, device=device)
+    with pytest.raises(ValueError):
+        loom.routed_combine(ids, torch.zeros(3, 2, device=device), torch.zeros(6, 8, device=device),
+                            out=torch.empty(3, 7, device=device))
+    with pytest.raises(ValueError):
+        loom.sum_guarded_rows(torch.zeros(4, 32, 4, device=device), 4, 4, 32, out=torch.empty(31, device=device))
+    with pytest.raises(ValueError):
+        loom.copy_f32(torch.zeros(10, device=device), out=torch.empty(9, device=device))
