@@ -19,7 +19,7 @@ namespace loom {
 // Schedules (records in flight, record size, load policy).  Each kernel
 // instantiation owns its schedule; the macros let a tuning build override it.
 #ifndef LOOM_GEMV_DEPTH
-#define LOOM_GEMV_DEPTH 4        // three 4 KiB records in flight per wave
+#define LOOM_GEMV_DEPTH 6        // five 1 KiB weight blocks in flight per wave
 #endif
 #ifndef LOOM_MFMA_DEPTH
 #define LOOM_MFMA_DEPTH 3        // two 4 KiB records in flight per wave
@@ -65,82 +65,69 @@ __device__ __forceinline__ int dot16(int4v a, int4v b, int acc) {
 }
 
 // ----------------------------------------------------------------------------
-// Single vector (batch == 1).  Rows are taken in tiles of kGemvTileRows; one
-// wave owns kGemvTilesPerWave consecutive tiles and streams them as one
-// sequence of records, so the read-ahead runs across tile boundaries and the
-// ring fills once per wave rather than once per tile.  A record is one 1 KiB
-// column block of k: the activation group each lane needs (16 bytes) and the
-// tile rows' weight groups at the same columns, so the activation fragment
-// is loaded once per record and reused by every row of the tile.  Rows past
-// the end of the matrix re-read the last row and their results are dropped,
-// so no load needs a row guard.  At the end of each tile the rows' int32
-// partials are summed across the wave (exact) into the lane that owns the
-// row in the wave's block; one coalesced epilogue then scales and stores
-// every row of the wave.
+// Single vector (batch == 1).  One wave owns a block of consecutive rows --
+// gemv_rows_per_wave(k): one row at the workloads' k of 8192, up to 64 for
+// short rows -- which is one contiguous stretch of the weight matrix, and
+// walks it row after row.  A record is one 1 KiB column block of one row plus
+// the activation group each lane needs at the same columns (16 bytes, reused
+// by every wave and kept in the caches), so the read-ahead runs across row
+// boundaries and the wave's weights stream in address order.  At the end of
+// each row its int32 partials are summed across the wave (exact) into the
+// lane that owns the row; one coalesced epilogue then scales and stores every
+// row of the wave.  Small blocks make many short waves, so the waves that
+// finish last at the end of the launch have little left to read.
 // ----------------------------------------------------------------------------
 struct GemvRecord {
-    int4v xv;
-    int4v wv[kGemvTileRows];
+    int4v xv, wv;
 };
 
-template <bool FULL, bool VEC16, int DEPTH>
-__global__ __launch_bounds__(kWave * kGemvWaves) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
+// ONE_ROW: rows_per_wave == 1, known at compile time.
+template <bool FULL, bool VEC16, int DEPTH, bool ONE_ROW>
+__global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
                                                         const int32_t *__restrict__ x,
                                                         const float *__restrict__ x_scale, int rows, int kw,
-                                                        float *__restrict__ out, int32_t *__restrict__ acc_out) {
+                                                        int rows_per_wave, float *__restrict__ out,
+                                                        int32_t *__restrict__ acc_out) {
     constexpr int kBlockWords = kWave * 4;
-    constexpr int TR = kGemvTileRows;
-    static_assert(TR * kGemvTilesPerWave <= kWave, "one lane per row of the wave's block");
+    if constexpr (ONE_ROW) rows_per_wave = 1;
     const int lane = lane_id();
-    const int row0 = (blockIdx.x * kGemvWaves + (int)(threadIdx.x / kWave)) * (TR * kGemvTilesPerWave);
-    if (row0 >= rows) return;  // a surplus wave of the last workgroup
-    const int wave_rows = min(TR * kGemvTilesPerWave, rows - row0);
-    const int tiles = (wave_rows + TR - 1) / TR;
-    const int records_per_tile = (kw + kBlockWords - 1) / kBlockWords;
+    const int row0 = blockIdx.x * rows_per_wave;
+    const int nrows = min(rows_per_wave, rows - row0);
+    const int records_per_row = (kw + kBlockWords - 1) / kBlockWords;
 
-    // producer cursor: tile, column block, and the tile's row pointers
-    int lblk = 0, ltile = 0;
-    const int32_t *wrow[TR];
-#pragma unroll
-    for (int r = 0; r < TR; ++r) wrow[r] = w + (int64_t)min(row0 + r, rows - 1) * kw;
+    // producer cursor (wave-uniform): the current row and the next column block
+    const int32_t *wrow = w + (int64_t)row0 * kw;
+    int lcol = 0;
     // consumer state
-    int acc[TR];
-#pragma unroll
-    for (int r = 0; r < TR; ++r) acc[r] = 0;
-    int cblk = 0, ctile = 0, mine = 0;
+    int acc = 0, crec = 0, crow = 0, mine = 0;
 
     pipelined<DEPTH, GemvRecord>(
-        tiles * records_per_tile,
+        nrows * records_per_row,
         [&]() {
-            const int c = lblk * kBlockWords + lane * 4;
             GemvRecord q;
+            const int c = lcol + lane * 4;
             q.xv = load_words<FULL, VEC16, false>(x, c, kw);
-#pragma unroll
-            for (int r = 0; r < TR; ++r) q.wv[r] = load_words<FULL, VEC16, true>(wrow[r], c, kw);
-            if (++lblk == records_per_tile) {
-                lblk = 0;
-                ++ltile;
-#pragma unroll
-                for (int r = 0; r < TR; ++r) wrow[r] = w + (int64_t)min(row0 + ltile * TR + r, rows - 1) * kw;
+            q.wv = load_words<FULL, VEC16, true>(wrow, c, kw);
+            if (lcol >= kw - kBlockWords) {
+                lcol = 0;
+                wrow += kw;
+            } else {
+                lcol += kBlockWords;
             }
             return q;
         },
         [&](const GemvRecord &q) {
-#pragma unroll
-            for (int r = 0; r < TR; ++r) acc[r] = dot16(q.wv[r], q.xv, acc[r]);
-            if (++cblk == records_per_tile) {
-#pragma unroll
-                for (int r = 0; r < TR; ++r) {
-                    const int total = wave_sum(acc[r]);
-                    if (lane == ctile * TR + r) mine = total;
-                    acc[r] = 0;
-                }
-                cblk = 0;
-                ++ctile;
+            acc = dot16(q.wv, q.xv, acc);
+            if (++crec == records_per_row) {
+                const int total = wave_sum(acc);
+                if (lane == crow) mine = total;
+                acc = 0;
+                crec = 0;
+                ++crow;
             }
         });
 
-    if (lane < wave_rows) {
+    if (lane < nrows) {
         const int row = row0 + lane;
         float y = (float)mine;
         y = y * w_scale[row];
@@ -325,12 +312,19 @@ hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w
                        (reinterpret_cast<uintptr_t>(x) % 16 == 0);
     if (batch == 1) {
         const bool full = k_words % (kWave * 4) == 0;
-        if (full && vec16)
-            i8_gemv_kernel<true, true, kGemvDepth><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, k_words, out, acc);
+        const int rpw = gemv_rows_per_wave(k_words);
+        if (full && vec16 && rpw == 1)
+            i8_gemv_kernel<true, true, kGemvDepth, true><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows,
+                                                                                    k_words, rpw, out, acc);
+        else if (full && vec16)
+            i8_gemv_kernel<true, true, kGemvDepth, false><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows,
+                                                                                     k_words, rpw, out, acc);
         else if (vec16)
-            i8_gemv_kernel<false, true, kGemvDepth><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, k_words, out, acc);
+            i8_gemv_kernel<false, true, kGemvDepth, false><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows,
+                                                                                      k_words, rpw, out, acc);
         else
-            i8_gemv_kernel<false, false, kGemvDepth><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, k_words, out, acc);
+            i8_gemv_kernel<false, false, kGemvDepth, false><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows,
+                                                                                       k_words, rpw, out, acc);
     } else {
         const bool full = k_words % (16 * kMfmaSteps) == 0;
         if (full && vec16)

@@ -35,29 +35,25 @@ constexpr int kTileRows = 8;
 constexpr int kRowSumsTilesPerWave = LOOM_ROW_SUMS_TILES_PER_WAVE;
 static_assert(kTileRows * kRowSumsTilesPerWave <= 64, "one lane per row of a wave's block");
 
-// Row tiles of the int8 kernels.  The v_dot4 GEMV takes tiles of 4 rows and
-// one wave streams TILES_PER_WAVE consecutive tiles; the MFMA kernel takes one
-// 16-row matrix-core tile per workgroup, whose KSPLIT waves split the k range
-// and combine their int32 partials through LDS in wave order (exact).
-// Tuning builds may override the macros.
-#ifndef LOOM_GEMV_TILE_ROWS
-#define LOOM_GEMV_TILE_ROWS 4
+// Blocking of the int8 kernels.  The v_dot4 GEMV gives each wave
+// gemv_rows_per_wave(k) consecutive rows, about 8 KiB of weights (one row at
+// k = 8192, at most 64 rows, one per lane of the result); the MFMA kernel
+// takes one 16-row matrix-core tile per workgroup, whose KSPLIT waves split
+// the k range and combine their int32 partials through LDS in wave order
+// (exact).  Tuning builds may override the macros.
+#ifndef LOOM_GEMV_WAVE_BYTES
+#define LOOM_GEMV_WAVE_BYTES 8192  // 1 row per wave at k = 8192: 6% faster than 4-row tiles
 #endif
-#ifndef LOOM_GEMV_TILES_PER_WAVE
-#define LOOM_GEMV_TILES_PER_WAVE 1
-#endif
-#ifndef LOOM_GEMV_WAVES
-#define LOOM_GEMV_WAVES 1     // waves per GEMV workgroup, each with its own tiles
-#endif
+constexpr int gemv_rows_per_wave(int64_t k_words) {
+    const int64_t r = k_words > 0 ? LOOM_GEMV_WAVE_BYTES / (4 * k_words) : 64;
+    return r < 1 ? 1 : r > 64 ? 64 : (int)r;
+}
 #ifndef LOOM_MFMA_KSPLIT
 #define LOOM_MFMA_KSPLIT 4    // 4 waves per 16-row tile: 7168 waves for 28672 rows
 #endif
 #ifndef LOOM_MFMA_STAGE
 #define LOOM_MFMA_STAGE 1     // weights reach the MFMA through a per-wave LDS tile
 #endif
-constexpr int kGemvTileRows = LOOM_GEMV_TILE_ROWS;
-constexpr int kGemvTilesPerWave = LOOM_GEMV_TILES_PER_WAVE;
-constexpr int kGemvWaves = LOOM_GEMV_WAVES;
 constexpr int kMfmaTileRows = 16;
 constexpr int kMfmaKSplit = LOOM_MFMA_KSPLIT;
 constexpr bool kMfmaStage = LOOM_MFMA_STAGE != 0;

@@ -66,14 +66,12 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 }
 
 // i8_dequant_dot(rows, k, batch): for one vector, one wave per block of
-// TILES_PER_WAVE GEMV tiles; for several, one workgroup per 16-row
+// gemv_rows_per_wave(k) rows; for several, one workgroup per 16-row
 // matrix-core tile whose KSPLIT waves split k (the LDS holds their partial
 // accumulators and the weight staging tiles).
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
-    if (w[2] == 1)
-        return set(c, ceil_div(w[0], int64_t(kGemvTileRows) * kGemvTilesPerWave * kGemvWaves),
-                   kSubgroupSize * kGemvWaves, 0);
+    if (w[2] == 1) return set(c, ceil_div(w[0], gemv_rows_per_wave(w[1] / 4)), kSubgroupSize, 0);
     return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * kMfmaKSplit,
                (kMfmaKSplit - 1) * mfma_col_tiles(w[2]) * 4 * kSubgroupSize * 4 +
                    (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));

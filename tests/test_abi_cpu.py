@@ -90,7 +90,7 @@ def test_launch_config_tiles(loom):
     seg = loom.launch_config_lookup("segment_sums")
     assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"][0] == 16384
     i8 = loom.launch_config_lookup("i8_dequant_dot")
-    assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 4096  # 4-row GEMV tiles
+    assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 16384  # one 8 KiB row per wave
     cfg = loom.launch_config_invoke(i8, [28672, 8192, 8])
     assert cfg["workgroups"][0] == 1792
     # 4 waves split k per 16-row tile; LDS: 3 waves' int32 partial tiles (1 KiB
