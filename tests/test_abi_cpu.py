@@ -260,3 +260,20 @@ def test_routed_combine_validation(loom, lib):
     assert loom.launch_config_invoke(tok, [256, 8, 1024])["workgroups"] == (256, 1, 1)  # 1024 columns per wave
     assert loom.launch_config_invoke(tok, [256, 8, 4096])["workgroups"] == (256, 4, 1)
     assert loom.launch_config_invoke(tok, [1, 32, 1028])["workgroups"] == (1, 2, 1)
+
+
+def test_header_is_plain_c_and_links(loom, tmp_path):
+    # include/loom.h is usable from C99 and C++ with no HIP or torch headers, and
+    # a C caller that names every declared entry point links against libloom.so
+    names = declared_symbols()
+    src = tmp_path / "use_loom.c"
+    src.write_text("#include \"loom.h\"\ntypedef void (*entry)(void);\nint main(void) {\n"
+                   "    entry table[] = {\n"
+                   + "".join(f"        (entry)&{n},\n" for n in names)
+                   + "    };\n    return table[0] != 0 && loom_version() > 0 ? 0 : 1;\n}\n")
+    inc = os.path.dirname(HEADER)
+    for compiler, std in (("gcc", "-std=c99"), ("g++", "-std=c++11")):
+        exe = tmp_path / f"use_loom_{compiler}"
+        lang = ["-x", "c++"] if compiler == "g++" else []
+        subprocess.run([compiler, std, "-Wall", "-Werror", "-pedantic", "-I", inc, *lang, str(src), "-x", "none",
+                        "-o", str(exe), loom.LIB_PATH, "-Wl,--allow-shlib-undefined"], check=True, capture_output=True)
