@@ -139,8 +139,10 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
 
 // ----------------------------------------------------------------------------
 // Several vectors (batch >= 2): the shared activations make this a dense
-// int8 contraction, so it runs on the matrix cores.  One wave owns a 16-row
-// tile and all k; each k step is one v_mfma_i32_16x16x64_i8:
+// int8 contraction, so it runs on the matrix cores.  One workgroup owns a
+// 16-row tile; its kMfmaKSplit waves each take a contiguous quarter of k (of
+// the records), and their int32 partial tiles are added in wave order at the
+// end (exact).  Each k step is one v_mfma_i32_16x16x64_i8:
 //   A (16 x 64, weights):  lane l holds 16 bytes of row (l & 15) at byte
 //                          offset 16*(l >> 4) of the 64-byte step;
 //   B (64 x 16, vectors):  lane l holds the same 16 byte positions of vector
