@@ -195,7 +195,8 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
         xrow[t] = x + (int64_t)min(n, batch - 1) * kw;
     }
     const int steps = (kw + kStepWords - 1) / kStepWords;
-    const int wave = threadIdx.x / kWave;
+    // the same in every lane: keeps the wave's k share and loop count scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     // this wave's contiguous share of the k records
     const int all_records = (steps + S - 1) / S;
     const int per_wave = (all_records + kMfmaKSplit - 1) / kMfmaKSplit;

@@ -34,6 +34,21 @@ constexpr int kTileRows = 8;
 #endif
 constexpr int kRowSumsTilesPerWave = LOOM_ROW_SUMS_TILES_PER_WAVE;
 static_assert(kTileRows * kRowSumsTilesPerWave <= 64, "one lane per row of a wave's block");
+// Rows of at least LOOM_ROW_SUMS_WIDE_RECORDS 256-float records (1 KiB each)
+// get a workgroup of their own: one wave per LOOM_ROW_SUMS_WIDE_RECORDS
+// records, at most kRowSumsWideMaxWaves (4 waves of 4 KiB for 4096 columns).
+// Shorter rows keep the wave-per-8-tiles kernel.  Returns the waves per row,
+// or 0 for the tiled kernel.
+#ifndef LOOM_ROW_SUMS_WIDE_RECORDS
+#define LOOM_ROW_SUMS_WIDE_RECORDS 4
+#endif
+constexpr int kRowSumsWideMaxWaves = 16;
+constexpr int row_sums_waves_per_row(int64_t cols) {
+    const int64_t records = (cols + 255) / 256;
+    if (records < LOOM_ROW_SUMS_WIDE_RECORDS) return 0;
+    const int64_t w = records / LOOM_ROW_SUMS_WIDE_RECORDS;
+    return w > kRowSumsWideMaxWaves ? kRowSumsWideMaxWaves : (int)w;
+}
 
 // Blocking of the int8 kernels.  The v_dot4 GEMV gives each wave
 // gemv_rows_per_wave(k) consecutive rows, about 8 KiB of weights (one row at

@@ -52,10 +52,12 @@ int geo_row_sum_tiles(const int64_t *w, loom_launch_config *c) {
     return set(c, 1, kSubgroupSize, 0);
 }
 
-// row_sums(rows, cols): one wave per block of TILES_PER_WAVE tiles of 8 rows
+// row_sums(rows, cols): long rows (row_sums_waves_per_row > 0) one workgroup
+// per row; short rows one wave per block of TILES_PER_WAVE tiles of 8 rows
 // (the last tile the tail).
 int geo_row_sums(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
+    if (const int waves = row_sums_waves_per_row(w[1])) return set(c, w[0], kSubgroupSize * waves, 0);
     return set(c, ceil_div(w[0], int64_t(kTileRows) * kRowSumsTilesPerWave), kSubgroupSize, 0);
 }
 

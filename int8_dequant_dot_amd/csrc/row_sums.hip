@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kWave) void row_sum_tiles_kernel(const float *__res
 }
 
 // ----------------------------------------------------------------------------
-// Streaming row sums.  One wave owns kRowSumsTilesPerWave consecutive tiles
+// Streaming row sums of short rows (under 1024 columns; longer rows take the
+// workgroup-per-row kernel below).  One wave owns kRowSumsTilesPerWave consecutive tiles
 // of 8 rows (the last tile of the matrix holds the rows mod 8 tail, so it is
 // the separate guarded tile of TUNE §Derive full tiles).  The wave's rows are
 // walked as one stream of records -- a record is
@@ -121,6 +122,56 @@ __global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict
     if (lane < nrows) out[row0 + lane] = mine;
 }
 
+// ----------------------------------------------------------------------------
+// Row sums of long rows (1024 columns and more).  One workgroup of
+// W = blockDim.x / 64 waves owns one row; wave w streams a contiguous share of
+// the row's records (the same 64 x VEC float records as above, about four per
+// wave) into a private partial, reduces it across the wave, and the W wave
+// totals are added in wave order (a fixed tree: the result does not depend on
+// timing).  A row needs no guard and there is no tail tile: every workgroup
+// has a whole row.  The many short waves (262,144 of 4 KiB for 65536 rows of
+// 4096 floats) keep the end of the launch short, and a matrix with few rows
+// still spreads over the GPU.
+// ----------------------------------------------------------------------------
+template <int VEC, bool FULL, int DEPTH>
+__global__ __launch_bounds__(kWave * kRowSumsWideMaxWaves) void row_sums_wide_kernel(const float *__restrict__ x,
+                                                                                   int cols, int64_t row_stride,
+                                                                                   float *__restrict__ out) {
+    typedef typename vec_of<VEC>::type V;
+    constexpr int kBlock = kWave * VEC;
+    const int lane = lane_id();
+    const int waves = blockDim.x / kWave;
+    // the same in every lane: keeps the wave's share and cursor in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int64_t row = blockIdx.x;
+    const int records = (cols + kBlock - 1) / kBlock;
+    const int per = (records + waves - 1) / waves;
+    const int first = min(records, wave * per);
+    const int n = min(records, first + per) - first;
+    const float *rp = x + row * row_stride;
+    int64_t lcol = (int64_t)first * kBlock;
+    const int lane_col = lane * VEC;
+    V acc = V(0.0f);
+    pipelined<DEPTH, V>(
+        n,
+        [&]() {
+            V v = V(0.0f);
+            if (FULL || lane_col < cols - lcol) v = load_stream(reinterpret_cast<const V *>(rp + lcol + lane_col));
+            lcol += kBlock;
+            return v;
+        },
+        [&](V v) { acc += v; });
+    const float total = wave_sum(fold<VEC>(acc));
+    __shared__ float part[kRowSumsWideMaxWaves];
+    if (lane == 0) part[wave] = total;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float sum = 0.0f;
+        for (int w = 0; w < waves; ++w) sum = sum + part[w];
+        out[row] = sum;
+    }
+}
+
 // Read-ahead depths (records in the ring).  Each kernel instantiation owns its
 // schedule; the macros let a tuning build override the defaults.
 #ifndef LOOM_ROW_SUM_TILES_DEPTH
@@ -129,7 +180,11 @@ __global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict
 #ifndef LOOM_ROW_SUMS_DEPTH
 #define LOOM_ROW_SUMS_DEPTH 8        // 7 KiB per wave in flight
 #endif
+#ifndef LOOM_ROW_SUMS_WIDE_DEPTH
+#define LOOM_ROW_SUMS_WIDE_DEPTH 4   // the whole 4-record share in flight; <= 128 VGPRs (16-wave groups)
+#endif
 constexpr int kRowSumTilesDepth = LOOM_ROW_SUM_TILES_DEPTH;
+constexpr int kRowSumsWideDepth = LOOM_ROW_SUMS_WIDE_DEPTH;
 constexpr int kRowSumsDepth = LOOM_ROW_SUMS_DEPTH;
 
 hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *values, int count,
@@ -145,6 +200,17 @@ hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int ro
                            int64_t row_stride, float *out, hipStream_t stream) {
     const dim3 grid(cfg.workgroups[0]), block(cfg.workgroup_size[0]);
     const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (row_stride % 4 == 0) && (cols % 4 == 0);
+    if (row_sums_waves_per_row(cols) > 0) {
+        if (vec4 && cols % (kWave * 4) == 0)
+            row_sums_wide_kernel<4, true, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);
+        else if (vec4)
+            row_sums_wide_kernel<4, false, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);
+        else if (cols % kWave == 0)
+            row_sums_wide_kernel<1, true, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);
+        else
+            row_sums_wide_kernel<1, false, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);
+        return hipGetLastError();
+    }
     if (vec4) {
         if (cols % (kWave * 4) == 0)
             row_sums_kernel<4, true, kRowSumsDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);

@@ -85,8 +85,15 @@ def test_launch_config_matches_oracle_geometry(loom):
 
 def test_launch_config_tiles(loom):
     rs = loom.launch_config_lookup("row_sums")
-    for rows in (0, 1, 7, 8, 9, 63, 64, 65, 65536, 65537):  # one wave per 8 tiles of 8 rows
-        assert loom.launch_config_invoke(rs, [rows, 4096])["workgroups"][0] == -(-rows // 64)
+    for rows in (0, 1, 7, 8, 9, 63, 64, 65, 65536, 65537):
+        # short rows: one wave per 8 tiles of 8 rows
+        assert loom.launch_config_invoke(rs, [rows, 256])["workgroups"][0] == -(-rows // 64)
+        assert loom.launch_config_invoke(rs, [rows, 768])["workgroup_size"][0] == 64
+        # long rows: a workgroup per row, one wave per 4 KiB of the row, at most 16
+        cfg = loom.launch_config_invoke(rs, [rows, 4096])
+        assert cfg["workgroups"][0] == rows and cfg["workgroup_size"][0] == 256
+    assert loom.launch_config_invoke(rs, [8, 1024])["workgroup_size"][0] == 64
+    assert loom.launch_config_invoke(rs, [8, 1 << 24])["workgroup_size"][0] == 1024
     seg = loom.launch_config_lookup("segment_sums")
     assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"][0] == 16384
     i8 = loom.launch_config_lookup("i8_dequant_dot")
@@ -277,3 +284,42 @@ def test_header_is_plain_c_and_links(loom, tmp_path):
         lang = ["-x", "c++"] if compiler == "g++" else []
         subprocess.run([compiler, std, "-Wall", "-Werror", "-pedantic", "-I", inc, *lang, str(src), "-x", "none",
                         "-o", str(exe), loom.LIB_PATH, "-Wl,--allow-shlib-undefined"], check=True, capture_output=True)
+
+
+def _kernel_metadata(lib_path, tmp_path):
+    """(name, private segment bytes, VGPRs) of every gfx950 kernel in the library: the
+    .hip_fatbin section holds one offload bundle per source file."""
+    llvm = "/opt/rocm/llvm/bin"
+    blob = tmp_path / "fatbin.bin"
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", lib_path, str(blob)], check=True)
+    data = blob.read_bytes()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = [m.start() for m in re.finditer(re.escape(magic), data)]
+    kernels = []
+    for i, st in enumerate(starts):
+        part, co = tmp_path / f"bundle{i}.bin", tmp_path / f"bundle{i}.co"
+        part.write_bytes(data[st:starts[i + 1] if i + 1 < len(starts) else len(data)])
+        subprocess.run([f"{llvm}/clang-offload-bundler", "--unbundle", "--type=o",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--input={part}", f"--output={co}"],
+                       check=True, capture_output=True)
+        notes = subprocess.run([f"{llvm}/llvm-readelf", "--notes", str(co)], check=True, capture_output=True,
+                               text=True).stdout
+        for entry in notes.split(".name:")[1:]:
+            name = entry.split()[0]
+            priv = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", entry).group(1))
+            vgpr = int(re.search(r"\.vgpr_count:\s+(\d+)", entry).group(1))
+            kernels.append((name, priv, vgpr))
+    return kernels
+
+
+def test_no_kernel_spills_to_scratch(loom, tmp_path):
+    # register spills go to per-lane scratch memory, an order of magnitude
+    # slower than the streaming loads these kernels are built around
+    kernels = _kernel_metadata(loom.LIB_PATH, tmp_path)
+    names = " ".join(n for n, _, _ in kernels)
+    for kernel in ("row_sums_kernel", "row_sums_wide_kernel", "segment_sums_kernel", "i8_gemv_kernel",
+                   "i8_mfma_kernel", "packed_dot_kernel", "packed_dot_spaced_kernel", "sum_guarded_rows_kernel",
+                   "routed_combine_kernel", "row_sum_tiles_kernel", "copy_f32_kernel"):
+        assert kernel in names, kernel
+    spilled = [(n, p) for n, p, _ in kernels if p != 0]
+    assert not spilled, spilled
