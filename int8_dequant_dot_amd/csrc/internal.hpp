@@ -30,10 +30,31 @@ int evaluate_launch(ExportId id, const int64_t *workload, loom_launch_config *ou
 constexpr int kTileRows = 8;
 // Consecutive tiles one row-sum wave streams (its read-ahead crosses them).
 #ifndef LOOM_ROW_SUMS_TILES_PER_WAVE
-#define LOOM_ROW_SUMS_TILES_PER_WAVE 8  // 64 rows per wave: 1024 waves for 65536 rows (1.7% faster than 1 tile)
+#define LOOM_ROW_SUMS_TILES_PER_WAVE 2  // 16 short rows per wave
 #endif
 constexpr int kRowSumsTilesPerWave = LOOM_ROW_SUMS_TILES_PER_WAVE;
 static_assert(kTileRows * kRowSumsTilesPerWave <= 64, "one lane per row of a wave's block");
+// Rows of 1 to kRowSumsNarrowMaxCols floats are packed several to a record:
+// returns log2 of the lanes per row (the smallest power of two L with
+// 4 L >= cols), or -1 for wider (or empty) rows.  A narrow wave streams
+// kRowSumsNarrowRecords records of 64 / L rows each.
+#ifndef LOOM_ROW_SUMS_NARROW_MAX_COLS
+#define LOOM_ROW_SUMS_NARROW_MAX_COLS 128
+#endif
+#ifndef LOOM_ROW_SUMS_NARROW_RECORDS
+#define LOOM_ROW_SUMS_NARROW_RECORDS 8
+#endif
+constexpr int kRowSumsNarrowRecords = LOOM_ROW_SUMS_NARROW_RECORDS;
+constexpr int row_sums_narrow_log2_lanes(int64_t cols) {
+    if (cols < 1 || cols > LOOM_ROW_SUMS_NARROW_MAX_COLS) return -1;
+    int k = 0;
+    while ((int64_t(4) << k) < cols) ++k;
+    return k;
+}
+constexpr int64_t row_sums_narrow_rows_per_wave(int64_t cols) {
+    return int64_t(64 >> row_sums_narrow_log2_lanes(cols)) * kRowSumsNarrowRecords;
+}
+
 // Rows of at least LOOM_ROW_SUMS_WIDE_RECORDS 256-float records (1 KiB each)
 // get a workgroup of their own: one wave per LOOM_ROW_SUMS_WIDE_RECORDS
 // records, at most kRowSumsWideMaxWaves (4 waves of 4 KiB for 4096 columns).

@@ -52,11 +52,14 @@ int geo_row_sum_tiles(const int64_t *w, loom_launch_config *c) {
     return set(c, 1, kSubgroupSize, 0);
 }
 
-// row_sums(rows, cols): long rows (row_sums_waves_per_row > 0) one workgroup
-// per row; short rows one wave per block of TILES_PER_WAVE tiles of 8 rows
-// (the last tile the tail).
+// row_sums(rows, cols): narrow rows (1-128 columns) several to a record, one
+// wave per kRowSumsNarrowRecords records; long rows (row_sums_waves_per_row > 0) one workgroup
+// per row; the others one wave per block of kRowSumsTilesPerWave tiles of 8
+// rows (the last tile the tail).
 int geo_row_sums(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
+    if (row_sums_narrow_log2_lanes(w[1]) >= 0)
+        return set(c, ceil_div(w[0], row_sums_narrow_rows_per_wave(w[1])), kSubgroupSize, 0);
     if (const int waves = row_sums_waves_per_row(w[1])) return set(c, w[0], kSubgroupSize * waves, 0);
     return set(c, ceil_div(w[0], int64_t(kTileRows) * kRowSumsTilesPerWave), kSubgroupSize, 0);
 }

@@ -172,13 +172,75 @@ __global__ __launch_bounds__(kWave * kRowSumsWideMaxWaves) void row_sums_wide_ke
     }
 }
 
+// ----------------------------------------------------------------------------
+// Row sums of narrow rows (1 to 128 columns).  A record packs R = 64 / L rows
+// side by side: lane l serves row l / L of the record and its columns
+// 4 (l mod L) .. 4 (l mod L) + 3, where L is the smallest power of two with
+// 4 L >= cols.  Each lane folds its (up to) four floats, and the first
+// log2(L) steps of the wave reduction -- which sum aligned groups of 2, 4,
+// ... lanes -- give every lane its row's total; the group's first lane
+// stores it.  A wave streams kRowSumsNarrowRecords records.  Lanes past the
+// last row or column still issue their load, from the wave's first element,
+// and the consumer drops the value, so every record is the same load
+// instructions on every path, the producer never waits on its own loads,
+// and the read-ahead keeps its partial waits.
+// ----------------------------------------------------------------------------
+template <int LOG2L>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (LOG2L >= 1) v = v + dpp<kDppQuadSwap1>(v);
+    if constexpr (LOG2L >= 2) v = v + dpp<kDppQuadSwap2>(v);
+    if constexpr (LOG2L >= 3) v = v + dpp<kDppHalfMirror>(v);
+    if constexpr (LOG2L >= 4) v = v + dpp<kDppMirror>(v);
+    if constexpr (LOG2L >= 5) v = v + swz16(v);
+    return v;
+}
+
+template <bool VEC4, int LOG2L, int DEPTH>
+__global__ __launch_bounds__(kWave) void row_sums_narrow_kernel(const float *__restrict__ x, int rows, int cols,
+                                                                int64_t row_stride, float *__restrict__ out) {
+    constexpr int L = 1 << LOG2L;
+    constexpr int R = kWave / L;
+    const int lane = lane_id();
+    const int sub = lane >> LOG2L;     // row within the record
+    const int q = lane & (L - 1);      // float4 column group within the row
+    const int row0 = blockIdx.x * (R * kRowSumsNarrowRecords);
+    const int left = rows - row0;      // rows of this wave's block that exist
+    const int nrec = min(kRowSumsNarrowRecords, (left + R - 1) / R);
+    const float *first = x + (int64_t)row0 * row_stride;
+    int lrec = 0, crec = 0;
+    pipelined<DEPTH, float4v>(
+        nrec,
+        [&]() {
+            const int lr = lrec * R + sub;  // row within the wave's block
+            const float *p = first + (int64_t)lr * row_stride + 4 * q;
+            float4v v;
+            if constexpr (VEC4) {
+                v = load_stream(reinterpret_cast<const float4v *>(lr < left && 4 * q < cols ? p : first));
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[c] = load_stream(lr < left && 4 * q + c < cols ? p + c : first);
+            }
+            ++lrec;
+            return v;
+        },
+        [&](float4v v) {
+            const int lr = crec * R + sub;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (!(lr < left && 4 * q + c < cols)) v[c] = 0.0f;
+            const float total = group_sum<LOG2L>((v.x + v.y) + (v.z + v.w));
+            if (q == 0 && lr < left) out[row0 + lr] = total;
+            ++crec;
+        });
+}
+
 // Read-ahead depths (records in the ring).  Each kernel instantiation owns its
 // schedule; the macros let a tuning build override the defaults.
 #ifndef LOOM_ROW_SUM_TILES_DEPTH
 #define LOOM_ROW_SUM_TILES_DEPTH 4   // one full tile (4 row pairs) in flight
 #endif
 #ifndef LOOM_ROW_SUMS_DEPTH
-#define LOOM_ROW_SUMS_DEPTH 8        // 7 KiB per wave in flight
+#define LOOM_ROW_SUMS_DEPTH 6        // 5 KiB per wave in flight
 #endif
 #ifndef LOOM_ROW_SUMS_WIDE_DEPTH
 #define LOOM_ROW_SUMS_WIDE_DEPTH 4   // the whole 4-record share in flight; <= 128 VGPRs (16-wave groups)
@@ -186,6 +248,23 @@ __global__ __launch_bounds__(kWave * kRowSumsWideMaxWaves) void row_sums_wide_ke
 constexpr int kRowSumTilesDepth = LOOM_ROW_SUM_TILES_DEPTH;
 constexpr int kRowSumsWideDepth = LOOM_ROW_SUMS_WIDE_DEPTH;
 constexpr int kRowSumsDepth = LOOM_ROW_SUMS_DEPTH;
+#ifndef LOOM_ROW_SUMS_NARROW_DEPTH
+#define LOOM_ROW_SUMS_NARROW_DEPTH 6
+#endif
+constexpr int kRowSumsNarrowDepth = LOOM_ROW_SUMS_NARROW_DEPTH;
+
+template <bool VEC4>
+static void launch_row_sums_narrow(dim3 grid, dim3 block, hipStream_t stream, const float *x, int rows, int cols,
+                                   int64_t row_stride, float *out) {
+    switch (row_sums_narrow_log2_lanes(cols)) {
+        case 0: row_sums_narrow_kernel<VEC4, 0, kRowSumsNarrowDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out); break;
+        case 1: row_sums_narrow_kernel<VEC4, 1, kRowSumsNarrowDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out); break;
+        case 2: row_sums_narrow_kernel<VEC4, 2, kRowSumsNarrowDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out); break;
+        case 3: row_sums_narrow_kernel<VEC4, 3, kRowSumsNarrowDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out); break;
+        case 4: row_sums_narrow_kernel<VEC4, 4, kRowSumsNarrowDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out); break;
+        default: row_sums_narrow_kernel<VEC4, 5, kRowSumsNarrowDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out); break;
+    }
+}
 
 hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *values, int count,
                                 const float *initial, float *sums, int32_t *final_row,
@@ -200,6 +279,13 @@ hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int ro
                            int64_t row_stride, float *out, hipStream_t stream) {
     const dim3 grid(cfg.workgroups[0]), block(cfg.workgroup_size[0]);
     const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (row_stride % 4 == 0) && (cols % 4 == 0);
+    if (row_sums_narrow_log2_lanes(cols) >= 0) {
+        if (vec4)
+            launch_row_sums_narrow<true>(grid, block, stream, x, rows, cols, row_stride, out);
+        else
+            launch_row_sums_narrow<false>(grid, block, stream, x, rows, cols, row_stride, out);
+        return hipGetLastError();
+    }
     if (row_sums_waves_per_row(cols) > 0) {
         if (vec4 && cols % (kWave * 4) == 0)
             row_sums_wide_kernel<4, true, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);

@@ -86,13 +86,17 @@ def test_launch_config_matches_oracle_geometry(loom):
 def test_launch_config_tiles(loom):
     rs = loom.launch_config_lookup("row_sums")
     for rows in (0, 1, 7, 8, 9, 63, 64, 65, 65536, 65537):
-        # short rows: one wave per 8 tiles of 8 rows
-        assert loom.launch_config_invoke(rs, [rows, 256])["workgroups"][0] == -(-rows // 64)
+        # short rows: one wave per 2 tiles of 8 rows
+        assert loom.launch_config_invoke(rs, [rows, 256])["workgroups"][0] == -(-rows // 16)
         assert loom.launch_config_invoke(rs, [rows, 768])["workgroup_size"][0] == 64
         # long rows: a workgroup per row, one wave per 4 KiB of the row, at most 16
         cfg = loom.launch_config_invoke(rs, [rows, 4096])
         assert cfg["workgroups"][0] == rows and cfg["workgroup_size"][0] == 256
     assert loom.launch_config_invoke(rs, [8, 1024])["workgroup_size"][0] == 64
+    # narrow rows: 64 / L rows per record (4 L >= cols), 8 records per wave
+    for cols, rows_per_wave in ((1, 512), (4, 512), (5, 256), (32, 64), (33, 32), (128, 16)):
+        assert loom.launch_config_invoke(rs, [100000, cols])["workgroups"][0] == -(-100000 // rows_per_wave), cols
+    assert loom.launch_config_invoke(rs, [100000, 129])["workgroups"][0] == -(-100000 // 16)  # tiled
     assert loom.launch_config_invoke(rs, [8, 1 << 24])["workgroup_size"][0] == 1024
     seg = loom.launch_config_lookup("segment_sums")
     assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"][0] == 16384

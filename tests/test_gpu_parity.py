@@ -120,7 +120,9 @@ def test_row_sum_tiles_long(loom, device):
 ROW_SHAPES = [(1, 1), (7, 3), (8, 256), (9, 4096), (17, 4096), (23, 1000), (33, 260), (64, 4096), (13, 4097),
               (5, 0), (3, 64), (41, 1024), (16, 8192), (70, 768), (66, 1023),
               # few long rows: a workgroup of up to 16 waves per row
-              (3, 300007), (2, 1 << 20), (5, 100000), (1, 65536 + 256 * 3)]
+              (3, 300007), (2, 1 << 20), (5, 100000), (1, 65536 + 256 * 3),
+              # narrow rows: several packed into each record
+              (70000, 4), (1000, 128), (999, 100), (513, 33), (65, 17), (4097, 2), (129, 64)]
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)

@@ -50,6 +50,24 @@ def test_row_sums_random_shapes(loom, device):
         assert np.all(np.abs(g.astype(np.float64) - d) <= bound), what
 
 
+def test_row_sums_narrow_random_shapes(loom, device):
+    # 1-128 columns: several rows packed into each 64-lane record
+    rng = np.random.default_rng(1008)
+    for case in range(40):
+        rows = int(rng.integers(1, 5000))
+        cols = int(rng.integers(1, 129))
+        pad = int(rng.choice([0, 0, 1, 4, 7]))
+        shift = int(rng.choice([0, 0, 1]))
+        full = synth.dense_rows(synth.DENSE.seed + 100 + case, 0, rows, cols + pad + shift)
+        x = full[:, shift:shift + cols]
+        g = _np(loom.row_sums(full.to(device)[:, shift:shift + cols]))
+        ref, d, a = oracle.row_sums(x.contiguous().numpy())
+        bound = REL_SUM * a + 1e-30
+        what = (case, rows, cols, pad, shift)
+        assert np.all(np.abs(g.astype(np.float64) - ref) <= bound), what
+        assert np.all(np.abs(g.astype(np.float64) - d) <= bound), what
+
+
 def test_row_sum_tiles_random_shapes(loom, device):
     rng = np.random.default_rng(1002)
     for case in range(40):
