@@ -71,6 +71,10 @@ constexpr int row_sums_waves_per_row(int64_t cols) {
     return w > kRowSumsWideMaxWaves ? kRowSumsWideMaxWaves : (int)w;
 }
 
+// Columns of one segment-sum wave: a segment of a wider matrix is spread over
+// ceil(cols / kSegmentBlockCols) waves (a 1 KiB record per row each).
+constexpr int kSegmentBlockCols = 256;
+
 // Blocking of the int8 kernels.  The v_dot4 GEMV gives each wave
 // gemv_rows_per_wave(k) consecutive rows, about 8 KiB of weights (one row at
 // k = 8192, at most 64 rows, one per lane of the result); the MFMA kernel

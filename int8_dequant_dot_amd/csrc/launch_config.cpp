@@ -64,10 +64,13 @@ int geo_row_sums(const int64_t *w, loom_launch_config *c) {
     return set(c, ceil_div(w[0], int64_t(kTileRows) * kRowSumsTilesPerWave), kSubgroupSize, 0);
 }
 
-// segment_sums(segments, cols): one wave per segment.
+// segment_sums(segments, cols): one wave per segment and block of
+// kSegmentBlockCols columns (at least one block, which also writes the
+// segment's tail count when there are no columns).
 int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
-    return set(c, w[0], kSubgroupSize, 0);
+    const int64_t blocks = w[1] > 0 ? ceil_div(w[1], kSegmentBlockCols) : 1;
+    return set2(c, w[0], blocks, kSubgroupSize, 0);
 }
 
 // i8_dequant_dot(rows, k, batch): for one vector, one wave per block of

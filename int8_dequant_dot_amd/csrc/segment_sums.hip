@@ -13,13 +13,18 @@ template <> struct seg_vec<4> { typedef float4v type; };
 // ----------------------------------------------------------------------------
 // TUNE §Keep one checked source for experiments (@sum_rows): each lane sums
 // its own column over the rows, one load and one add per row, in row order.
-// Here one wave owns one segment; a lane owns VEC adjacent columns of a
-// 64*VEC-column block (256 columns = one 1 KiB coalesced record per row for
-// VEC = 4) and walks the segment's rows in order -- the full 8-row tiles and
-// then the tail, which are consecutive -- with the next rows read ahead.  No
-// cross-lane reduction is needed, and every column's sum is the same in-order
-// f32 recurrence a serial loop computes.  Segments with bad offsets are
-// reported in-band and read nothing.
+// Here one wave owns one segment and one block of kSegmentBlockCols columns
+// (blockIdx.y picks the block, so a wide matrix spreads a segment over several
+// waves without changing any column's order).  A lane owns VEC adjacent
+// columns of each 64*VEC-column part of the block (one 1 KiB coalesced record
+// per row for VEC = 4) and walks the segment's rows in order -- the full
+// 8-row tiles and then the tail, which are consecutive -- with the next rows
+// read ahead.  No cross-lane reduction is needed, and every column's sum is
+// the same in-order f32 recurrence a serial loop computes.  Lanes past the
+// last column load from the start of the row instead (always inside the
+// matrix) and never store, so every lane issues the same loads and the
+// read-ahead keeps its partial waits.  Segments with bad offsets are reported
+// in-band and read nothing.
 // ----------------------------------------------------------------------------
 template <int VEC, bool FULL, int DEPTH>
 __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__restrict__ x, int64_t total_rows,
@@ -30,30 +35,31 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
     constexpr int kBlock = kWave * VEC;
     const int lane = lane_id();
     const int64_t s = blockIdx.x;
+    const int block_first = blockIdx.y * kSegmentBlockCols;
+    const int block_end = min(cols, block_first + kSegmentBlockCols);
     const int64_t begin = offsets[s];
     const int64_t end = offsets[s + 1];
     float *o = out + s * cols;
 
     if (!(begin >= 0 && begin <= end && end <= total_rows)) {
-        for (int c = lane; c < cols; c += kWave) o[c] = __builtin_nanf("");
-        if (lane == 0 && tail_counts) tail_counts[s] = -1;
+        for (int c = block_first + lane; c < block_end; c += kWave) o[c] = __builtin_nanf("");
+        if (lane == 0 && blockIdx.y == 0 && tail_counts) tail_counts[s] = -1;
         return;
     }
     const int64_t length = end - begin;
-    if (lane == 0 && tail_counts) tail_counts[s] = (int32_t)(length & (kTileRows - 1));
+    if (lane == 0 && blockIdx.y == 0 && tail_counts) tail_counts[s] = (int32_t)(length & (kTileRows - 1));
 
-    for (int cb = 0; cb < cols; cb += kBlock) {
+    for (int cb = block_first; cb < block_end; cb += kBlock) {
         const int c = cb + lane * VEC;
         const bool active = FULL || c < cols;
         // Row base of the next load (wave-uniform) plus the lane's column.
         const float *rp = x + begin * cols + cb;
-        const int lane_col = lane * VEC;
+        const int lane_col = active ? lane * VEC : -cb;  // inactive lanes read the row's first columns
         V acc = V(0.0f);
         pipelined<DEPTH, V>(
             length,
             [&]() {
-                V v = V(0.0f);
-                if (active) v = load_stream(reinterpret_cast<const V *>(rp + lane_col));
+                const V v = load_stream(reinterpret_cast<const V *>(rp + lane_col));
                 rp += cols;
                 return v;
             },
@@ -70,7 +76,7 @@ constexpr int kSegmentDepth = LOOM_SEGMENT_SUMS_DEPTH;
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
                                const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
                                hipStream_t stream) {
-    const dim3 grid(cfg.workgroups[0]), block(cfg.workgroup_size[0]);
+    const dim3 grid(cfg.workgroups[0], cfg.workgroups[1]), block(cfg.workgroup_size[0]);
     const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0) &&
                       (cols % 4 == 0);
     if (vec4) {

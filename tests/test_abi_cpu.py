@@ -99,7 +99,9 @@ def test_launch_config_tiles(loom):
     assert loom.launch_config_invoke(rs, [100000, 129])["workgroups"][0] == -(-100000 // 16)  # tiled
     assert loom.launch_config_invoke(rs, [8, 1 << 24])["workgroup_size"][0] == 1024
     seg = loom.launch_config_lookup("segment_sums")
-    assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"][0] == 16384
+    assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"] == (16384, 1, 1)
+    assert loom.launch_config_invoke(seg, [100, 1000])["workgroups"] == (100, 4, 1)  # a wave per 256 columns
+    assert loom.launch_config_invoke(seg, [5, 0])["workgroups"] == (5, 1, 1)  # still writes the tail counts
     i8 = loom.launch_config_lookup("i8_dequant_dot")
     assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 16384  # one 8 KiB row per wave
     cfg = loom.launch_config_invoke(i8, [28672, 8192, 8])

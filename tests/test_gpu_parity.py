@@ -180,6 +180,9 @@ SEG_CASES = [
     ([40, 0, 23], 512),       # two column blocks
     ([0, 0], 256),
     ([1000, 3, 511], 256),    # long segments through the steady loop
+    ([3, 40, 0, 9], 1000),    # four column blocks, the last partial (128-bit path)
+    ([2, 300], 2050),         # nine blocks, 32-bit path
+    ([0, 5], 0),              # no columns: only the tail counts
 ]
 
 
