@@ -127,10 +127,14 @@ int loom_row_sum_tiles(const float *values, int64_t rows_alloc, int64_t count,
  * Streaming row sums (TUNE §Derive full tiles, §Give each motif its own     *
  * schedule, §Read-ahead; CTRL §Pipeline reads ahead of ordered computation) *
  *     out[r] = sum_{c < cols} x[r*row_stride + c],   0 <= r < rows          *
- * Rows are processed in full 8-row tiles plus one guarded tail tile; each   *
- * row is streamed with coalesced loads read ahead of the accumulation and   *
- * finished by a wave64 reduction.  f32 accumulation; the summation order    *
- * inside a row is a tree (error <= 1e-5 * sum|x| for the documented sizes). *
+ * Every row is streamed with coalesced loads read ahead of the             *
+ * accumulation and finished by cross-lane reductions; how rows map to the   *
+ * GPU depends on their width: 1-128 floats are packed several to a 64-lane  *
+ * record; 129-1023 floats run in full 8-row tiles plus one guarded tail     *
+ * tile; a row of 1024 floats or more gets a workgroup of its own whose      *
+ * wave totals are added in wave order.  f32 accumulation; the summation     *
+ * order inside a row is a fixed tree, the same on every call (error         *
+ * <= 1e-5 * sum|x| for the documented sizes).                               *
  *   x          : f32, device, 4-byte aligned (16-byte alignment of x and    *
  *                row_stride % 4 == 0 select 128-bit loads)                  *
  *   rows, cols : 0 <= rows < 2^31, 0 <= cols < 2^31                         *
