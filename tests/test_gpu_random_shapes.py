@@ -160,3 +160,24 @@ def test_routed_combine_random_shapes(loom, device):
         g = _np(loom.routed_combine(ids.to(device), weights.to(device), payload.to(device)))
         ref = oracle.routed_combine(ids.numpy(), weights.numpy(), payload.numpy())[0]
         assert np.array_equal(_bits(g), _bits(ref)), (case, tokens, routes, hidden, missing)
+
+
+def test_repeat_calls_are_bitwise_identical(loom, device):
+    # every reduction order is fixed by the kernel's structure, not by timing:
+    # repeated calls on the same inputs give the same bits
+    x = synth.dense_rows(synth.DENSE.seed, 0, 3000, 4096).to(device)
+    narrow = synth.dense_rows(synth.DENSE.seed, 0, 20000, 37).to(device)
+    skinny = synth.dense_rows(synth.DENSE.seed, 0, 3, 1 << 20).to(device)
+    lengths = torch.from_numpy(np.random.default_rng(9).integers(0, 300, 200)).to(torch.int64)
+    off = synth.segment_offsets(lengths)
+    seg = synth.segment_rows(synth.SEGMENTS.seed, 0, int(off[-1]), 768).to(device)
+    w = loom.pack_int8(synth.i8_rows(5, synth.S_W, 0, 300, 8192).to(device))
+    v8 = loom.pack_int8(synth.i8_rows(5, synth.S_X, 0, 8, 8192).to(device))
+    ws = synth.scales(5, synth.S_WSCALE, 0, 300).to(device)
+    runs = []
+    for _ in range(2):
+        runs.append([loom.row_sums(x), loom.row_sums(narrow), loom.row_sums(skinny),
+                     loom.segment_sums(seg, off.to(device))[0],
+                     loom.i8_dequant_dot(w, ws, v8[:1]), loom.i8_dequant_dot(w, ws, v8)])
+    for a, b in zip(*runs):
+        assert np.array_equal(_bits(_np(a)), _bits(_np(b)))
