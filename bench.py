@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,10 +42,16 @@ KERNEL_SOURCES = ("device_common.hpp", "internal.hpp", "row_sums.hip")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the row-sum kernel's sources with comments and blank space removed,
+    so the recorded traffic stays valid across comment edits and lapses on any
+    change to the code."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "int8_dequant_dot_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "int8_dequant_dot_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,6 +1,11 @@
-// row_sums.hip -- the tiled 32-lane row sum and the streaming row sum on gfx950.
+// row_sums.hip -- the tiled 32-lane row sum and the streaming row sums on gfx950.
 //
-// TUNE = "Tune loop unrolling and pipelining" (Loom pages).
+// TUNE = "Tune loop unrolling and pipelining" (Loom pages).  The streaming
+// row sums pick one of three mappings by row width (row_sums_narrow_log2_lanes
+// and row_sums_waves_per_row choose; the launch table uses the same rules):
+//   1-128 floats      several rows packed into each 64-lane record
+//   129-1023 floats   one wave per 2 full 8-row tiles, the last tile the tail
+//   1024+ floats      one workgroup per row, its columns split over 1-16 waves
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -52,11 +57,11 @@ __global__ __launch_bounds__(kWave) void row_sum_tiles_kernel(const float *__res
 }
 
 // ----------------------------------------------------------------------------
-// Streaming row sums of short rows (under 1024 columns; longer rows take the
-// workgroup-per-row kernel below).  One wave owns kRowSumsTilesPerWave consecutive tiles
-// of 8 rows (the last tile of the matrix holds the rows mod 8 tail, so it is
-// the separate guarded tile of TUNE §Derive full tiles).  The wave's rows are
-// walked as one stream of records -- a record is
+// Streaming row sums of rows of 129-1023 floats.  One wave owns
+// kRowSumsTilesPerWave consecutive tiles of 8 rows (the last tile of the
+// matrix holds the rows mod 8 tail, so it is the separate guarded tile of
+// TUNE §Derive full tiles).  The wave's rows are walked as one stream of
+// records -- a record is
 // 64 lanes x VEC contiguous floats of one row (1 KiB for VEC = 4) -- so the
 // read-ahead crosses row boundaries without draining.  Each lane folds its
 // floats into a private partial; at the end of a row the wave64 reduction
