@@ -60,7 +60,8 @@ int geo_row_sums(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
     if (row_sums_narrow_log2_lanes(w[1]) >= 0)
         return set(c, ceil_div(w[0], row_sums_narrow_rows_per_wave(w[1])), kSubgroupSize, 0);
-    if (const int waves = row_sums_waves_per_row(w[1])) return set(c, w[0], kSubgroupSize * waves, 0);
+    if (const int waves = row_sums_waves_per_row(w[1]))
+        return set(c, w[0], kSubgroupSize * waves, 4 * kRowSumsWideMaxWaves);  // LDS: the wave totals
     return set(c, ceil_div(w[0], int64_t(kTileRows) * kRowSumsTilesPerWave), kSubgroupSize, 0);
 }
 

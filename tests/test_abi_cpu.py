@@ -92,6 +92,7 @@ def test_launch_config_tiles(loom):
         # long rows: a workgroup per row, one wave per 4 KiB of the row, at most 16
         cfg = loom.launch_config_invoke(rs, [rows, 4096])
         assert cfg["workgroups"][0] == rows and cfg["workgroup_size"][0] == 256
+        assert cfg["workgroup_storage_bytes"] == 64  # 16 wave totals in LDS
     assert loom.launch_config_invoke(rs, [8, 1024])["workgroup_size"][0] == 64
     # narrow rows: 64 / L rows per record (4 L >= cols), 8 records per wave
     for cols, rows_per_wave in ((1, 512), (4, 512), (5, 256), (32, 64), (33, 32), (128, 16)):
