@@ -127,7 +127,7 @@ int loom_row_sum_tiles(const float *values, int64_t rows_alloc, int64_t count,
  * Streaming row sums (TUNE §Derive full tiles, §Give each motif its own     *
  * schedule, §Read-ahead; CTRL §Pipeline reads ahead of ordered computation) *
  *     out[r] = sum_{c < cols} x[r*row_stride + c],   0 <= r < rows          *
- * Every row is streamed with coalesced loads read ahead of the             *
+ * Every row is streamed with coalesced loads read ahead of the              *
  * accumulation and finished by cross-lane reductions; how rows map to the   *
  * GPU depends on their width: 1-128 floats are packed several to a 64-lane  *
  * record; 129-1023 floats run in full 8-row tiles plus one guarded tail     *
@@ -139,6 +139,8 @@ int loom_row_sum_tiles(const float *values, int64_t rows_alloc, int64_t count,
  *                row_stride % 4 == 0 select 128-bit loads)                  *
  *   rows, cols : 0 <= rows < 2^31, 0 <= cols < 2^31                         *
  *   row_stride : elements between row starts, row_stride >= cols            *
+ *                (LOOM_ERR_SHAPE); 4 * rows * row_stride must fit in an     *
+ *                int64 (LOOM_ERR_RANGE)                                     *
  *   out        : f32[rows], device                                          *
  * ------------------------------------------------------------------------ */
 int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t row_stride,
