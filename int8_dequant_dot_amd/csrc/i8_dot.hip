@@ -101,7 +101,9 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
     // consumer state
     int acc = 0, crec = 0, crow = 0, mine = 0;
 
-    pipelined<DEPTH, GemvRecord>(
+    // a row of 8192 bytes is 8 records, most of them in the drain: the straight
+    // drain measured about 3 % faster here
+    pipelined<DEPTH, GemvRecord, true>(
         nrows * records_per_row,
         [&]() {
             GemvRecord q;

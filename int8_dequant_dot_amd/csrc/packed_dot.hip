@@ -107,7 +107,8 @@ __device__ __forceinline__ void packed_dot_spaced_wave(const int32_t *__restrict
     const uint16_t *sp = scales + base;
     const float4v *ap = reinterpret_cast<const float4v *>(rhs);
     const int act = lane % streams;
-    pipelined<DEPTH, SpacedRecord<OPL>>(
+    // the straight drain measured about 2 % faster here (128 records)
+    pipelined<DEPTH, SpacedRecord<OPL>, true>(
         count,
         [&]() {
             SpacedRecord<OPL> q;
