@@ -10,7 +10,7 @@
 namespace loom {
 
 #ifndef LOOM_ROUTED_DEPTH
-#define LOOM_ROUTED_DEPTH 6   // payload rows in flight per wave
+#define LOOM_ROUTED_DEPTH 8   // ring depth: up to 7 payload rows in flight per wave
 #endif
 constexpr int kRoutedDepth = LOOM_ROUTED_DEPTH;
 constexpr int kRoutedVecs = kRoutedColumnsPerWave / (kWave * 4);  // float4s per lane per route
