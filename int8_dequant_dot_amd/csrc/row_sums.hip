@@ -242,13 +242,13 @@ __global__ __launch_bounds__(kWave) void row_sums_narrow_kernel(const float *__r
 // Read-ahead depths (records in the ring).  Each kernel instantiation owns its
 // schedule; the macros let a tuning build override the defaults.
 #ifndef LOOM_ROW_SUM_TILES_DEPTH
-#define LOOM_ROW_SUM_TILES_DEPTH 4   // one full tile (4 row pairs) in flight
+#define LOOM_ROW_SUM_TILES_DEPTH 4   // the ring holds one full tile (4 row pairs)
 #endif
 #ifndef LOOM_ROW_SUMS_DEPTH
 #define LOOM_ROW_SUMS_DEPTH 6        // 5 KiB per wave in flight
 #endif
 #ifndef LOOM_ROW_SUMS_WIDE_DEPTH
-#define LOOM_ROW_SUMS_WIDE_DEPTH 4   // the whole 4-record share in flight; <= 128 VGPRs (16-wave groups)
+#define LOOM_ROW_SUMS_WIDE_DEPTH 4   // 3 of a wave's 4 records issued at once; <= 128 VGPRs (16-wave groups)
 #endif
 constexpr int kRowSumTilesDepth = LOOM_ROW_SUM_TILES_DEPTH;
 constexpr int kRowSumsWideDepth = LOOM_ROW_SUMS_WIDE_DEPTH;
