@@ -293,6 +293,103 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
 }
 
 
+// ----------------------------------------------------------------------------
+// Nine to sixteen vectors, rows of 4 to 8 KiB streamed whole (the choice of
+// kernel is i8_rows_chunks).  One workgroup of 16 waves
+// per CU walks 16-row tiles (tile t, t + gridDim.x, ...).  Wave w holds row w
+// of the next tile in registers -- its k bytes, one contiguous 1 KiB per load
+// instruction -- while the current tile is consumed, then stores it into an
+// LDS tile with 16-byte chunk c of row r at slot c ^ r of that row, so both the
+// row-wise stores and the 16-row fragment reads fall on distinct banks.
+// After a barrier, wave w multiplies the 16 rows by the vectors over its
+// 1/16 of k (CHUNKS steps of 64 bytes, in the A/B/D layouts of the kernel
+// above; its vector fragments are loaded once and stay in registers for every
+// tile), writes its int32 partial tile to LDS, and after a second barrier the
+// first 256 threads each add one output's 16 partials (exact) and apply the
+// epilogue.  The barriers wait for LDS only: the next tile's row loads stay in
+// flight across them.  Every wave of a workgroup runs the same tiles, so all
+// reach every barrier.
+// ----------------------------------------------------------------------------
+template <int CHUNKS, bool VEC16>
+__global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
+    const int32_t *__restrict__ w, const float *__restrict__ w_scale, const int32_t *__restrict__ x,
+    const float *__restrict__ x_scale, int rows, int kw, int batch, float *__restrict__ out,
+    int32_t *__restrict__ acc_out) {
+    static_assert(CHUNKS >= 1 && CHUNKS <= kI8RowsMaxChunks, "k is 1 to 8 KiB per row");
+    constexpr int kUnits = CHUNKS * kWave;  // 16-byte chunks per row (kw = 256 * CHUNKS words)
+    __shared__ int4v tile[kMfmaTileRows * kUnits];
+    __shared__ int partial[kI8RowsWaves][4][kWave];
+    const int lane = lane_id();
+    // the same in every lane: keeps the wave's k share and row scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int ntiles = (rows + kMfmaTileRows - 1) / kMfmaTileRows;
+    const int m = lane & 15, g = lane >> 4;
+
+    // this wave's vector fragments, k steps wave * CHUNKS .. + CHUNKS; every
+    // lane loads a valid (clamped) vector and columns past the batch are zeroed
+    int4v bfrag[CHUNKS];
+    const int32_t *xrow = x + (int64_t)min(m, batch - 1) * kw;
+#pragma unroll
+    for (int s = 0; s < CHUNKS; ++s) {
+        const int4v v = load_words<true, VEC16, false>(xrow, (wave * CHUNKS + s) * 16 + g * 4, kw);
+        bfrag[s] = m < batch ? v : int4v{0, 0, 0, 0};
+    }
+
+    int4v rowbuf[CHUNKS];
+    auto load_row = [&](int t) {
+        // rows past the end load the last row; their outputs are never stored
+        const int32_t *src = w + (int64_t)min(t * kMfmaTileRows + wave, rows - 1) * kw;
+#pragma unroll
+        for (int j = 0; j < CHUNKS; ++j) rowbuf[j] = load_words<true, VEC16, true>(src, (j * kWave + lane) * 4, kw);
+    };
+
+    int t = blockIdx.x;
+    if (t < ntiles) load_row(t);
+    for (; t < ntiles; t += gridDim.x) {
+#pragma unroll
+        for (int j = 0; j < CHUNKS; ++j) {
+            const int c = j * kWave + lane;
+            tile[wave * kUnits + (c ^ wave)] = rowbuf[j];
+        }
+        if (t + (int)gridDim.x < ntiles) load_row(t + gridDim.x);
+        __syncthreads();
+        int4v acc = int4v{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < CHUNKS; ++s) {
+            const int c = (wave * CHUNKS + s) * 4 + g;
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(tile[m * kUnits + (c ^ m)], bfrag[s], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) partial[wave][i][lane] = acc[i];
+        __syncthreads();
+        if (threadIdx.x < kMfmaTileRows * 16) {
+            // output (r, n) of the tile sits in lane 16 (r / 4) + n, slot r % 4, of every partial
+            const int r = threadIdx.x >> 4, n = threadIdx.x & 15;
+            int sum = 0;
+            for (int v = 0; v < kI8RowsWaves; ++v) sum += partial[v][r & 3][(r >> 2) * 16 + n];
+            const int row = t * kMfmaTileRows + r;
+            if (n < batch && row < rows) {
+                float y = (float)sum;
+                y = y * w_scale[row];
+                if (x_scale) y = y * x_scale[n];
+                out[(int64_t)row * batch + n] = y;
+                if (acc_out) acc_out[(int64_t)row * batch + n] = sum;
+            }
+        }
+    }
+}
+
+template <int CHUNKS>
+static void launch_mfma_rows(dim3 grid, bool vec16, hipStream_t stream, const int32_t *w, const float *w_scale,
+                             const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
+                             int32_t *acc) {
+    const dim3 block(kWave * kI8RowsWaves);
+    if (vec16)
+        i8_mfma_rows_kernel<CHUNKS, true><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+    else
+        i8_mfma_rows_kernel<CHUNKS, false><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+}
+
 template <bool FULL, bool VEC16>
 static void launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
                         const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
@@ -315,6 +412,17 @@ hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w
     const dim3 grid(cfg.workgroups[0]), block(cfg.workgroup_size[0]);
     const bool vec16 = (k_words % 4 == 0) && (reinterpret_cast<uintptr_t>(w) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+    switch (i8_rows_chunks(rows, 4 * (int64_t)k_words, batch)) {
+        case 1: launch_mfma_rows<1>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
+        case 2: launch_mfma_rows<2>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
+        case 3: launch_mfma_rows<3>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
+        case 4: launch_mfma_rows<4>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
+        case 5: launch_mfma_rows<5>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
+        case 6: launch_mfma_rows<6>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
+        case 7: launch_mfma_rows<7>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
+        case 8: launch_mfma_rows<8>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
+        default: break;
+    }
     if (batch == 1) {
         const bool full = k_words % (kWave * 4) == 0;
         const int rpw = gemv_rows_per_wave(k_words);

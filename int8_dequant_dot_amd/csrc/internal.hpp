@@ -123,6 +123,34 @@ constexpr int kRoutedColumnsPerWave = LOOM_ROUTED_COLUMNS;
 
 // 16-vector column tiles the MFMA kernel needs for a batch.
 constexpr int mfma_col_tiles(int64_t batch) { return batch <= 16 ? 1 : batch <= 32 ? 2 : 4; }
+
+// The row-streaming MFMA kernel: one workgroup of 16 waves per CU (an MI355X
+// has 256) walks 16-row tiles, each wave streaming one whole row per tile
+// into LDS.  It serves batches of 9 to 16 vectors when k is a multiple of
+// 1024 from 4096 to 8192 (4 to 8 chunks of 1 KiB per row).  There the
+// tile-per-workgroup kernel above slows down as the batch grows (at k = 8192:
+// 42.8 against 37.4 us for 16 vectors), while below 9 vectors the two are
+// within a few percent and below k = 4096 the short rows leave the row kernel
+// waiting on its two barriers per tile (k = 1024: 65 against 48-57 us).
+// LDS: the 16-row tile and the 16 waves' int32 partial tiles.
+#ifndef LOOM_I8_ROWS_MIN_BATCH
+#define LOOM_I8_ROWS_MIN_BATCH 9
+#endif
+constexpr int kI8RowsWaves = 16;
+constexpr int kI8RowsGroups = 256;
+#ifndef LOOM_I8_ROWS_MIN_CHUNKS
+#define LOOM_I8_ROWS_MIN_CHUNKS 4
+#endif
+constexpr int kI8RowsMaxChunks = 8;
+constexpr int i8_rows_chunks(int64_t rows, int64_t k, int64_t batch) {
+    return (batch >= LOOM_I8_ROWS_MIN_BATCH && batch <= 16 && rows >= 16 && k % 1024 == 0 &&
+            k >= 1024 * LOOM_I8_ROWS_MIN_CHUNKS && k <= 1024 * kI8RowsMaxChunks)
+               ? (int)(k / 1024)
+               : 0;
+}
+constexpr uint32_t i8_rows_lds_bytes(int chunks) {
+    return 16u * 1024u * (uint32_t)chunks + (uint32_t)kI8RowsWaves * 4u * 64u * 4u;
+}
 constexpr int kMaxBatch = 64;
 constexpr int64_t kMaxK = 131068;
 

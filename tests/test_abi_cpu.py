@@ -113,6 +113,17 @@ def test_launch_config_tiles(loom):
     assert cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096
     assert loom.launch_config_invoke(i8, [28672, 8192, 64])["workgroup_storage_bytes"] == 3 * 4 * 1024 + 4 * 4096
     assert loom.launch_config_invoke(i8, [17, 64, 2])["workgroups"][0] == 2
+    # 9-16 vectors, k a multiple of 1024 from 4096 to 8192: one 16-wave
+    # workgroup per CU walks the 16-row tiles; LDS: the tile (16 rows x k
+    # bytes) and the 16 waves' partial tiles
+    cfg = loom.launch_config_invoke(i8, [28672, 8192, 16])
+    assert cfg["workgroups"][0] == 256 and cfg["workgroup_size"] == (1024, 1, 1)
+    assert cfg["workgroup_storage_bytes"] == 16 * 8192 + 16 * 1024
+    assert loom.launch_config_invoke(i8, [100, 5120, 9])["workgroups"][0] == 7
+    assert loom.launch_config_invoke(i8, [100, 5120, 9])["workgroup_storage_bytes"] == 16 * 5120 + 16 * 1024
+    for shape in ([28672, 8192, 8], [100, 1000, 12], [100, 9216, 12], [15, 4096, 12], [100, 4096, 17],
+                  [100, 3072, 16]):
+        assert loom.launch_config_invoke(i8, shape)["workgroup_size"] == (256, 1, 1), shape  # tile-per-workgroup kernel
     t = loom.launch_config_lookup("row_sum_tiles")
     assert loom.launch_config_invoke(t, [63])["workgroups"] == (1, 1, 1)
     assert loom.launch_config_invoke(t, [63])["workgroup_size"] == (64, 1, 1)
@@ -325,7 +336,7 @@ def test_no_kernel_spills_to_scratch(loom, tmp_path):
     kernels = _kernel_metadata(loom.LIB_PATH, tmp_path)
     names = " ".join(n for n, _, _ in kernels)
     for kernel in ("row_sums_kernel", "row_sums_wide_kernel", "segment_sums_kernel", "i8_gemv_kernel",
-                   "i8_mfma_kernel", "packed_dot_kernel", "packed_dot_spaced_kernel", "sum_guarded_rows_kernel",
+                   "i8_mfma_kernel", "i8_mfma_rows_kernel", "packed_dot_kernel", "packed_dot_spaced_kernel", "sum_guarded_rows_kernel",
                    "routed_combine_kernel", "row_sum_tiles_kernel", "copy_f32_kernel"):
         assert kernel in names, kernel
     spilled = [(n, p) for n, p, _ in kernels if p != 0]

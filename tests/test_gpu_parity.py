@@ -276,6 +276,11 @@ I8_CASES = [
     (1, 4, 1), (7, 4, 1), (8, 1024, 1), (9, 1028, 1), (17, 8192, 1), (33, 1040, 1), (100, 2112, 1), (5, 0, 1),
     (3, 64, 2), (15, 256, 3), (16, 260, 8), (17, 1000, 8), (100, 8192, 8), (33, 64, 16), (40, 512, 17),
     (20, 1024, 32), (18, 320, 33), (16, 4096, 64), (1, 4, 2), (31, 8, 5),
+    # 9-16 vectors with k a multiple of 1024 from 4096 to 8192: the row-streaming
+    # kernel (one workgroup per CU walking 16-row tiles; 8197 rows give 513
+    # tiles, so workgroups take two or three tiles each)
+    (16, 4096, 9), (17, 4096, 16), (100, 6144, 12), (300, 8192, 16), (47, 5120, 11), (8197, 4096, 16),
+    (1000, 7168, 13),
 ]
 
 
@@ -284,6 +289,23 @@ def test_i8_dequant_dot(loom, device, rows, k, batch):
     w, x, ws, xs = _i8_case(100 + rows + k + batch, rows, k, batch, with_xscale=(batch % 2 == 0))
     gy, gacc = _run_i8(loom, device, w, x, ws, xs)
     _check_i8(gy, gacc, w, x, ws, xs, f"{rows}x{k}x{batch}")
+
+
+@pytest.mark.parametrize("batch", [8, 16])
+def test_i8_unaligned_operands(loom, device, batch):
+    # weights and vectors starting 4 bytes past a 16-byte boundary: the kernels
+    # read them as single words instead of 16-byte groups
+    rows, k = 70, 4096
+    w, x, ws, xs = _i8_case(77 + batch, rows, k, batch)
+    wbuf = torch.zeros(rows * k // 4 + 1, dtype=torch.int32, device=device)
+    xbuf = torch.zeros(batch * k // 4 + 1, dtype=torch.int32, device=device)
+    wp = wbuf[1:].view(rows, k // 4)
+    xp = xbuf[1:].view(batch, k // 4)
+    wp.copy_(loom.pack_int8(w.to(device)))
+    xp.copy_(loom.pack_int8(x.to(device)))
+    assert wp.data_ptr() % 16 == 4 and xp.data_ptr() % 16 == 4
+    y, acc = loom.i8_dequant_dot(wp, ws.to(device), xp, xs.to(device), want_acc=True)
+    _check_i8(_np(y), _np(acc), w, x, ws, xs, f"unaligned {rows}x{k}x{batch}")
 
 
 @pytest.mark.parametrize("batch", [1, 8])
