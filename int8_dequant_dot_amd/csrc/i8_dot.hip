@@ -383,11 +383,16 @@ template <int CHUNKS>
 static void launch_mfma_rows(dim3 grid, bool vec16, hipStream_t stream, const int32_t *w, const float *w_scale,
                              const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
                              int32_t *acc) {
-    const dim3 block(kWave * kI8RowsWaves);
-    if (vec16)
-        i8_mfma_rows_kernel<CHUNKS, true><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
-    else
-        i8_mfma_rows_kernel<CHUNKS, false><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+    // only the row lengths i8_rows_chunks admits are instantiated
+    if constexpr (CHUNKS >= LOOM_I8_ROWS_MIN_CHUNKS) {
+        const dim3 block(kWave * kI8RowsWaves);
+        if (vec16)
+            i8_mfma_rows_kernel<CHUNKS, true><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out,
+                                                                          acc);
+        else
+            i8_mfma_rows_kernel<CHUNKS, false><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch,
+                                                                           out, acc);
+    }
 }
 
 template <bool FULL, bool VEC16>
