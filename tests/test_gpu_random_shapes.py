@@ -117,6 +117,27 @@ def test_i8_dequant_dot_random_shapes(loom, device):
         assert np.array_equal(_bits(_np(y)), _bits(ry)), what
 
 
+def test_i8_dequant_dot_row_kernel_random_shapes(loom, device):
+    # 9-16 vectors at k = 4-8 KiB: the row-streaming kernel, over tile counts
+    # below and above one workgroup per CU
+    rng = np.random.default_rng(1009)
+    for case in range(12):
+        rows = int(rng.integers(16, 4600))  # past 4096 some workgroups take two tiles
+        k = 1024 * int(rng.integers(4, 9))
+        batch = int(rng.integers(9, 17))
+        seed = 7000 + case
+        w = synth.i8_rows(seed, synth.S_W, 0, rows, k)
+        x = synth.i8_rows(seed, synth.S_X, 0, batch, k)
+        ws = synth.scales(seed, synth.S_WSCALE, 0, rows)
+        xs = synth.scales(seed, synth.S_XSCALE, 0, batch) if case % 2 else None
+        y, acc = loom.i8_dequant_dot(loom.pack_int8(w.to(device)), ws.to(device), loom.pack_int8(x.to(device)),
+                                     None if xs is None else xs.to(device), want_acc=True)
+        ry, racc = oracle.i8_dequant_dot(w.numpy(), ws.numpy(), x.numpy(), None if xs is None else xs.numpy())
+        what = (case, rows, k, batch)
+        assert np.array_equal(_np(acc), racc), what
+        assert np.array_equal(_bits(_np(y)), _bits(ry)), what
+
+
 def test_packed_dot_random_shapes(loom, device):
     rng = np.random.default_rng(1005)
     shapes = [(int(rng.integers(1, 3000)), int(rng.choice([1, 2, 3, 16, 64, 100])), int(rng.integers(0, 40)))
