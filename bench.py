@@ -102,7 +102,7 @@ def graph_us(fn, reps: int):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--segments", action="store_true", help="also time segment_sums on 16384 segments")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
