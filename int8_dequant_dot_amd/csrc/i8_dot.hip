@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
     const int lane = lane_id();
     // the same in every lane: keeps the wave's k share and row scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    const int ntiles = (rows + kMfmaTileRows - 1) / kMfmaTileRows;
+    const int ntiles = (int)(((int64_t)rows + kMfmaTileRows - 1) / kMfmaTileRows);
     const int m = lane & 15, g = lane >> 4;
 
     // this wave's vector fragments, k steps wave * CHUNKS .. + CHUNKS; every
