@@ -13,7 +13,11 @@
  * ---------------------------------
  *  - Return LOOM_OK (0) or a negative loom_status.  All argument checks run on
  *    the host before anything is enqueued; on error nothing is launched and no
- *    output is touched.
+ *    output is touched.  Sizes and counts are checked first (LOOM_ERR_RANGE,
+ *    LOOM_ERR_SHAPE); a call with nothing to do (no rows, elements, segments,
+ *    outputs or tokens) then returns LOOM_OK without looking at its pointers;
+ *    otherwise required pointers (LOOM_ERR_NULL) and then alignment
+ *    (LOOM_ERR_ALIGN) are checked.
  *  - Data pointers are device pointers (HIP allocations of the current device,
  *    e.g. a torch tensor's data_ptr()).  The caller owns all memory.  The
  *    library allocates no device memory and keeps no pointer after returning.
@@ -99,7 +103,7 @@ int loom_launch_config_invoke(uint32_t token, const uint64_t *workload_bits,
  * 256 work-items; work-items at or beyond n touch nothing, so out[n..] is   *
  * left as it was (1009 elements run on 4 workgroups).                       *
  *   in, out : f32[n], device, 4-byte aligned; may be NULL only when n == 0  *
- *   n       : 0 <= n <= 2^31 * 255 (LOOM_ERR_RANGE otherwise)               *
+ *   n       : 0 <= n <= 255 * (2^31 - 1) (LOOM_ERR_RANGE otherwise)         *
  * ------------------------------------------------------------------------ */
 int loom_copy_f32(const float *in, float *out, int64_t n, void *stream);
 
@@ -155,12 +159,12 @@ int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t row_stride
  * Each column accumulates its rows in row order in f32, so every output is  *
  * the in-order recurrence (an empty segment gives +0.0).                    *
  *   x           : f32[total_rows][cols], device, row-major, 4-byte aligned  *
- *   total_rows  : rows in x, 0 <= total_rows < 2^40                         *
+ *   total_rows  : rows in x, 0 <= total_rows <= 2^40                        *
  *   offsets     : int64[segments+1], device, CSR row offsets.  A segment    *
  *                 with offsets[s] > offsets[s+1], offsets[s] < 0 or         *
  *                 offsets[s+1] > total_rows reads nothing; its outputs are  *
  *                 set to NaN and its tail count to -1.                      *
- *   segments    : 0 <= segments < 2^31                                      *
+ *   segments    : 0 <= segments < 2^31 - 1                                  *
  *   cols        : 0 <= cols <= 2^20                                         *
  *   out         : f32[segments][cols], device                               *
  *   tail_counts : int32[segments], device, or NULL                          *
@@ -208,8 +212,9 @@ int loom_i8_dequant_dot(const int32_t *w, const float *w_scale, const int32_t *x
  *             streams)                                                      *
  *   streams : 1 <= streams < 2^31                                           *
  *   initial : f32[outputs] or NULL                                          *
- *   records : records allocated; 0 <= count <= records (LOOM_ERR_RANGE)     *
- *   outputs : 0 <= outputs <= 2^31 * 255                                    *
+ *   records : records allocated; 0 <= count <= records, count < 2^31, and   *
+ *             4 * records * outputs fits in an int64 (LOOM_ERR_RANGE)     *
+ *   outputs : 0 <= outputs <= 255 * (2^31 - 1)                              *
  *   out     : f32[outputs]                                                  *
  * ------------------------------------------------------------------------ */
 int loom_packed_dot(const int32_t *fields, const uint16_t *scales, const float *rhs, int64_t streams,
