@@ -77,8 +77,10 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 // i8_dequant_dot(rows, k, batch): for one vector, one wave per block of
 // gemv_rows_per_wave(k) rows; for 9 to 16 vectors and k a multiple of 1024
 // from 4096 to 8192, one 16-wave workgroup per CU (at most one per 16-row
-// tile) that walks the tiles; otherwise one workgroup per 16-row matrix-core tile whose
-// KSPLIT waves split k (the LDS holds their partial accumulators and the
+// tile) that walks the tiles; for more than 16 vectors, one workgroup per
+// 16-row tile with one wave per 16-vector column tile (LDS: two 16-row x
+// 256-byte record slots); otherwise one workgroup per 16-row matrix-core tile
+// whose KSPLIT waves split k (the LDS holds their partial accumulators and the
 // weight staging tiles).
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
@@ -88,9 +90,10 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
         return set(c, tiles < kI8RowsGroups ? tiles : kI8RowsGroups, kSubgroupSize * kI8RowsWaves,
                    i8_rows_lds_bytes(chunks));
     }
+    if (w[2] > 16)
+        return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * mfma_col_tiles(w[2]), 2 * 16 * 256);
     return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * kMfmaKSplit,
-               (kMfmaKSplit - 1) * mfma_col_tiles(w[2]) * 4 * kSubgroupSize * 4 +
-                   (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));
+               (kMfmaKSplit - 1) * 4 * kSubgroupSize * 4 + (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));
 }
 
 // packed_dot(outputs, count, streams): 256 lanes per workgroup, one output

@@ -111,7 +111,12 @@ def test_launch_config_tiles(loom):
     # each) + 4 per-wave 16x256 B weight staging tiles
     assert cfg["workgroup_size"] == (256, 1, 1)
     assert cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096
-    assert loom.launch_config_invoke(i8, [28672, 8192, 64])["workgroup_storage_bytes"] == 3 * 4 * 1024 + 4 * 4096
+    # more than 16 vectors: one wave per 16-vector column tile; LDS: two 16-row x 256 B record slots
+    cfg = loom.launch_config_invoke(i8, [28672, 8192, 64])
+    assert cfg["workgroups"][0] == 1792 and cfg["workgroup_size"] == (256, 1, 1)
+    assert cfg["workgroup_storage_bytes"] == 2 * 4096
+    cfg = loom.launch_config_invoke(i8, [100, 1000, 17])
+    assert cfg["workgroups"][0] == 7 and cfg["workgroup_size"] == (128, 1, 1)
     assert loom.launch_config_invoke(i8, [17, 64, 2])["workgroups"][0] == 2
     # 9-16 vectors, k a multiple of 1024 from 4096 to 8192: one 16-wave
     # workgroup per CU walks the 16-row tiles; LDS: the tile (16 rows x k
@@ -121,9 +126,9 @@ def test_launch_config_tiles(loom):
     assert cfg["workgroup_storage_bytes"] == 16 * 8192 + 16 * 1024
     assert loom.launch_config_invoke(i8, [100, 5120, 9])["workgroups"][0] == 7
     assert loom.launch_config_invoke(i8, [100, 5120, 9])["workgroup_storage_bytes"] == 16 * 5120 + 16 * 1024
-    for shape in ([28672, 8192, 8], [100, 1000, 12], [100, 9216, 12], [15, 4096, 12], [100, 4096, 17],
-                  [100, 3072, 16]):
-        assert loom.launch_config_invoke(i8, shape)["workgroup_size"] == (256, 1, 1), shape  # tile-per-workgroup kernel
+    for shape in ([28672, 8192, 8], [100, 1000, 12], [100, 9216, 12], [15, 4096, 12], [100, 3072, 16]):
+        cfg = loom.launch_config_invoke(i8, shape)  # the tile-per-workgroup kernel
+        assert cfg["workgroup_size"] == (256, 1, 1) and cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096, shape
     t = loom.launch_config_lookup("row_sum_tiles")
     assert loom.launch_config_invoke(t, [63])["workgroups"] == (1, 1, 1)
     assert loom.launch_config_invoke(t, [63])["workgroup_size"] == (64, 1, 1)
@@ -336,7 +341,7 @@ def test_no_kernel_spills_to_scratch(loom, tmp_path):
     kernels = _kernel_metadata(loom.LIB_PATH, tmp_path)
     names = " ".join(n for n, _, _ in kernels)
     for kernel in ("row_sums_kernel", "row_sums_wide_kernel", "segment_sums_kernel", "i8_gemv_kernel",
-                   "i8_mfma_kernel", "i8_mfma_rows_kernel", "packed_dot_kernel", "packed_dot_spaced_kernel", "sum_guarded_rows_kernel",
+                   "i8_mfma_kernel", "i8_mfma_rows_kernel", "i8_mfma_cols_kernel", "packed_dot_kernel", "packed_dot_spaced_kernel", "sum_guarded_rows_kernel",
                    "routed_combine_kernel", "row_sum_tiles_kernel", "copy_f32_kernel"):
         assert kernel in names, kernel
     spilled = [(n, p) for n, p, _ in kernels if p != 0]

@@ -6,7 +6,7 @@ kernels only (no host synchronisation, allocation or memset on the stream),
 and no kernel depends on state left by an earlier launch.  Between replays
 the outputs are poisoned and unrelated eager work runs on the same stream.
 One case per kernel variant (narrow, tiled and long-row row sums; GEMV and
-both MFMA kernels; one-output and four-output packed dot; ...).
+all three MFMA kernels; one-output and four-output packed dot; ...).
 """
 import numpy as np
 import pytest
@@ -46,7 +46,7 @@ def _cases(loom, dev):
         so = torch.empty(7, cols, device=dev)
         st = torch.empty(7, dtype=torch.int32, device=dev)
         c[f"segment_sums_{cols}"] = (lambda xs=xs, off=off, so=so, st=st: loom.segment_sums(xs, off, so, st))
-    for batch in (1, 8, 16):
+    for batch in (1, 8, 16, 40):
         w = loom.pack_int8(synth.i8_rows(5, synth.S_W, 0, 300, 8192, dev))
         v = loom.pack_int8(synth.i8_rows(5, synth.S_X, 0, batch, 8192, dev))
         ws = synth.scales(5, synth.S_WSCALE, 0, 300, dev)
@@ -71,6 +71,7 @@ def _cases(loom, dev):
 
 CASE_NAMES = ["copy_f32", "row_sum_tiles", "row_sums_narrow", "row_sums_tiled", "row_sums_long",
               "segment_sums_256", "segment_sums_300", "i8_dequant_dot_b1", "i8_dequant_dot_b8", "i8_dequant_dot_b16",
+              "i8_dequant_dot_b40",
               "packed_dot_2048", "packed_dot_65856", "sum_guarded_rows", "routed_combine"]
 
 

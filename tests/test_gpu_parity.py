@@ -281,6 +281,8 @@ I8_CASES = [
     # tiles, so workgroups take two or three tiles each)
     (16, 4096, 9), (17, 4096, 16), (100, 6144, 12), (300, 8192, 16), (47, 5120, 11), (8197, 4096, 16),
     (1000, 7168, 13),
+    # more than 16 vectors: one wave per 16-vector column tile, partial records and tiles
+    (33, 8192, 48), (17, 1000, 20), (50, 260, 64), (300, 4096, 40),
 ]
 
 
@@ -291,7 +293,7 @@ def test_i8_dequant_dot(loom, device, rows, k, batch):
     _check_i8(gy, gacc, w, x, ws, xs, f"{rows}x{k}x{batch}")
 
 
-@pytest.mark.parametrize("batch", [8, 16])
+@pytest.mark.parametrize("batch", [8, 16, 33])
 def test_i8_unaligned_operands(loom, device, batch):
     # weights and vectors starting 4 bytes past a 16-byte boundary: the kernels
     # read them as single words instead of 16-byte groups
