@@ -10,13 +10,14 @@ the 256 MB last-level cache: every launch reads HBM.
 
 Prints one JSON line.  `value` is total algorithmic bytes per step / time per
 step, timed over K back-to-back steps (phase A).  `roofline` is for the
-dominant kernel (row_sums): its algorithmic bytes / its mean duration over K
-back-to-back launches between two HIP events on the launch stream (phase B; the
-start event queued behind one untimed launch, so the timed ones never wait for
-the host).  `cpu_baseline` is
+dominant kernel (row_sums): its algorithmic bytes / its mean duration over five
+repetitions of K back-to-back launches between two HIP events on the launch
+stream (phase B; each start event queued behind one untimed launch, so the
+timed ones never wait for the host).  `cpu_baseline` is
 the CPU oracle on the same workload on one core (also used to check the outputs);
 `cpu_baseline_all_cores` runs the same oracle calls over row blocks on every
-usable host core.  `parts` gives each kernel's mean, median and minimum time; the
+usable host core.  `parts` gives each kernel's mean time and the median and
+minimum of its five per-repetition means; the
 pages' own launch-bound shapes (the 63x32 tile, the 1009-element copy, the
 guarded 63x32x4 rows, the 2048x128 packed dot, the 256-token routed combines)
 add `us_graph`, the device time per call inside a HIP graph of back-to-back calls.
@@ -208,33 +209,31 @@ def main():
     # buffer of its ring), so the device is still busy when the host queues the
     # first timed launch: the timed launches run back to back, without the idle
     # gap of an empty queue waiting for the host's first call.
-    per_kernel_ms, per_launch_ms = [], []
+    # Five repetitions of the K launches give the median and minimum of the
+    # per-launch mean; `us` is the mean over all five repetitions.
+    REPS = 5
+    per_kernel_ms, per_rep_ms = [], []
     for _, _, fn in kernels:
-        torch.cuda.synchronize()
-        fn(-1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(K):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        per_kernel_ms.append(e0.elapsed_time(e1) / K)
-        # the same K launches with an event between each pair, for median and min
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-        fn(-1)
-        ev[0].record(stream)
-        for i in range(K):
-            fn(i)
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        per_launch_ms.append(sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(K)))
+        reps = []
+        for _ in range(REPS):
+            torch.cuda.synchronize()
+            fn(-1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(K):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) / K)
+        per_kernel_ms.append(sum(reps) / REPS)
+        per_rep_ms.append(sorted(reps))
 
     parts = {}
-    for (name, nbytes, _), ms, each in zip(kernels, per_kernel_ms, per_launch_ms):
+    for (name, nbytes, _), ms, reps in zip(kernels, per_kernel_ms, per_rep_ms):
         gbs = nbytes / (ms * 1e-3) / 1e9
         parts[name] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
                        "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                       "us_median": round(each[len(each) // 2] * 1e3, 2), "us_min": round(each[0] * 1e3, 2)}
+                       "us_median": round(reps[REPS // 2] * 1e3, 2), "us_min": round(reps[0] * 1e3, 2)}
     # useful int8 operations of the batched product (2 per multiply-add) against
     # the dense int8 MFMA peak: the product is HBM-bound by a wide margin
     ops5 = 2 * R5 * K5 * B5
