@@ -34,7 +34,14 @@ namespace loom {
 #define LOOM_MFMA_STEPS 4        // k steps (KiB of weights per wave) per record
 #endif
 #ifndef LOOM_I8_COLS_DEPTH
-#define LOOM_I8_COLS_DEPTH 4     // 256 B weight records in flight per wave, 17-64 vectors
+#define LOOM_I8_COLS_DEPTH 3     // records in flight per wave, 17-64 vectors
+#endif
+#ifndef LOOM_I8_COLS_STAGGER
+// First record of workgroup b: (b * STAGGER) mod records.  With every
+// workgroup at the same column offset the 17-64 vector shapes ran 2-12 %
+// slower; a stagger of 1 was up to 20 % slower at k = 8192, 5 the best of
+// 1, 5 and 11 overall.
+#define LOOM_I8_COLS_STAGGER 5
 #endif
 constexpr int kGemvDepth = LOOM_GEMV_DEPTH;
 constexpr int kMfmaDepth = LOOM_MFMA_DEPTH;
@@ -384,91 +391,112 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// More than 16 vectors: one workgroup per 16-row tile with one wave per
-// 16-vector column tile (2 or 4).  The waves split each 256-byte weight record
-// of the tile (16 rows; each wave loads 4 or 8 rows of it, whole 256-byte
-// pieces) and store it into one of two LDS slots, swizzled as in the kernels
-// above; after a barrier each wave multiplies the whole record by its own
-// vectors (4 k steps).  Every wave thus covers the full k for its columns and
-// stores its outputs directly.  A barrier per record is enough with two slots:
-// a wave can only overwrite a slot after every wave has passed the next
-// record's barrier, that is, after all of them have finished reading it.
-// Compared with the tile kernel holding 2 or 4 column tiles of fragments per
-// wave, the registers stay at one column tile and the occupancy is kept.
+// More than 16 vectors: one workgroup of NT * RG waves owns RG * RT 16-row
+// tiles (64 rows at the default shapes).  Wave (group, c) multiplies the RT
+// tiles of its row group by the 16-vector column tile c.  The waves split
+// each 256-byte weight record of the workgroup's rows (each loads SHARE
+// instructions of 4 rows x 256 B, whole 256-byte pieces) and store it into
+// one of two LDS slots, swizzled as in the kernels above; after a barrier
+// each wave multiplies its RT tiles of the record by its own vector
+// fragments (4 k steps), which it loads once per record for all RT tiles, so
+// the vectors are read from the caches once per RT * RG tiles instead of
+// once per tile.  Every wave covers the full k for its outputs and stores them
+// directly.  A barrier per record is enough with two slots: a wave can only
+// overwrite a slot after every wave has passed the next record's barrier,
+// that is, after all of them have finished reading it.
 // ----------------------------------------------------------------------------
-template <int NT> struct ColsRecord {
-    int4v a[4 / NT];   // this wave's share of the record: 4 / NT loads of 4 rows x 256 B
+template <int SHARE> struct ColsRecord {
+    int4v a[SHARE];    // this wave's share of the record: SHARE loads of 4 rows x 256 B
     int4v b[4];        // its vector fragments for the record's 4 k steps
 };
 
-template <bool FULL, bool VEC16, int NT, int DEPTH>
-__global__ __launch_bounds__(kWave * NT) void i8_mfma_cols_kernel(
+template <bool FULL, bool VEC16, int NT, int RT, int RG, int DEPTH>
+__global__ __launch_bounds__(kWave * NT * RG) void i8_mfma_cols_kernel(
     const int32_t *__restrict__ w, const float *__restrict__ w_scale, const int32_t *__restrict__ x,
     const float *__restrict__ x_scale, int rows, int kw, int batch, float *__restrict__ out,
     int32_t *__restrict__ acc_out) {
     static_assert(NT == 2 || NT == 4, "two or four column tiles");
-    constexpr int kShare = 4 / NT;
-    constexpr int kRecordWords = 64;  // 256 bytes of each of the 16 rows
-    __shared__ int4v stage[2][kMfmaTileRows * 16];
+    constexpr int kWaves = NT * RG;
+    constexpr int kRows = kMfmaTileRows * RT * RG;  // rows per workgroup
+    constexpr int kShare = kRows / (4 * kWaves);     // 4-row loads per wave and record
+    static_assert(kShare >= 1 && kShare * 4 * kWaves == kRows, "the waves split the record evenly");
+    constexpr int kRecordWords = 64;  // 256 bytes of each row
+    __shared__ int4v stage[2][kRows * 16];
     const int lane = lane_id();
-    // the same in every lane: the wave's column tile and row share stay scalar
+    // the same in every lane: the wave's column tile, row group and row share stay scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int ct = wave % NT, group = wave / NT;
     const int m = lane & 15, g = lane >> 4;
-    const int row0 = blockIdx.x * kMfmaTileRows;
+    const int row0 = blockIdx.x * kRows;
     // staged loads: instruction i reads rows 4 (wave * kShare + i) .. + 3, 256 contiguous bytes each
     const int srow = lane >> 4, schunk = lane & 15;
     const int32_t *wsrc[kShare];
 #pragma unroll
     for (int i = 0; i < kShare; ++i)
         wsrc[i] = w + (int64_t)min(row0 + (wave * kShare + i) * 4 + srow, rows - 1) * kw;
-    const int n = wave * 16 + m;  // this lane's vector
+    const int n = ct * 16 + m;  // this lane's vector
     const bool live = n < batch;
     const int32_t *xrow = x + (int64_t)min(n, batch - 1) * kw;
     const int records = (kw + kRecordWords - 1) / kRecordWords;
 
-    int lrec = 0, crec = 0;
-    int4v acc = int4v{0, 0, 0, 0};
-    pipelined<DEPTH, ColsRecord<NT>>(
+    // Workgroup b walks the records from (b * STAGGER) mod records, wrapping
+    // around: the sums are exact int32, so the order of the records does not
+    // change them, and the workgroups' concurrent loads then fall on different
+    // column offsets of their rows.
+    int lrec = records > 0 ? (int)(((int64_t)blockIdx.x * LOOM_I8_COLS_STAGGER) % records) : 0;
+    int crec = 0;
+    int4v acc[RT];
+#pragma unroll
+    for (int j = 0; j < RT; ++j) acc[j] = int4v{0, 0, 0, 0};
+    pipelined<DEPTH, ColsRecord<kShare>>(
         records,
         [&]() {
-            ColsRecord<NT> q;
+            ColsRecord<kShare> q;
 #pragma unroll
             for (int i = 0; i < kShare; ++i)
                 q.a[i] = load_words<FULL, VEC16, true>(wsrc[i], lrec * kRecordWords + schunk * 4, kw);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 q.b[s] = load_words<FULL, VEC16, false>(xrow, lrec * kRecordWords + s * 16 + g * 4, kw);
-            ++lrec;
+            lrec = lrec + 1 == records ? 0 : lrec + 1;
             return q;
         },
-        [&](const ColsRecord<NT> &q) {
+        [&](const ColsRecord<kShare> &q) {
             int4v *slot = stage[crec & 1];
 #pragma unroll
             for (int i = 0; i < kShare; ++i) {
                 const int r = (wave * kShare + i) * 4 + srow;
-                slot[16 * r + (schunk ^ r)] = q.a[i];
+                slot[16 * r + (schunk ^ (r & 15))] = q.a[i];
             }
             __syncthreads();
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(slot[16 * m + ((4 * s + g) ^ m)], live_b(q.b[s], live),
-                                                            acc, 0, 0, 0);
+            for (int s = 0; s < 4; ++s) {
+                const int4v b = live_b(q.b[s], live);
+#pragma unroll
+                for (int j = 0; j < RT; ++j) {
+                    const int r = (group * RT + j) * kMfmaTileRows + m;
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(slot[16 * r + ((4 * s + g) ^ m)], b, acc[j], 0, 0,
+                                                                   0);
+                }
+            }
             ++crec;
         });
 
     if (live) {
         const float xs = x_scale ? x_scale[n] : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = row0 + 4 * g + i;
-            if (row < rows) {
-                float y = (float)acc[i];
-                y = y * w_scale[row];
-                if (x_scale) y = y * xs;
-                out[(int64_t)row * batch + n] = y;
-                if (acc_out) acc_out[(int64_t)row * batch + n] = acc[i];
+        for (int j = 0; j < RT; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = row0 + (group * RT + j) * kMfmaTileRows + 4 * g + i;
+                if (row < rows) {
+                    float y = (float)acc[j][i];
+                    y = y * w_scale[row];
+                    if (x_scale) y = y * xs;
+                    out[(int64_t)row * batch + n] = y;
+                    if (acc_out) acc_out[(int64_t)row * batch + n] = acc[j][i];
+                }
             }
-        }
     }
 }
 
@@ -476,11 +504,12 @@ template <bool FULL, bool VEC16>
 static void launch_mfma_cols(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
                              const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
                              int32_t *acc) {
+    // the shapes below are the ones the launch geometry (i8_cols_*) describes
     if (mfma_col_tiles(batch) == 2)
-        i8_mfma_cols_kernel<FULL, VEC16, 2, kI8ColsDepth>
+        i8_mfma_cols_kernel<FULL, VEC16, 2, i8_cols_row_tiles(2), i8_cols_row_groups(2), kI8ColsDepth>
             <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
     else
-        i8_mfma_cols_kernel<FULL, VEC16, 4, kI8ColsDepth>
+        i8_mfma_cols_kernel<FULL, VEC16, 4, i8_cols_row_tiles(4), i8_cols_row_groups(4), kI8ColsDepth>
             <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
 }
 

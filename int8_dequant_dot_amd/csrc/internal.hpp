@@ -124,6 +124,32 @@ constexpr int kRoutedColumnsPerWave = LOOM_ROUTED_COLUMNS;
 // 16-vector column tiles the MFMA kernel needs for a batch.
 constexpr int mfma_col_tiles(int64_t batch) { return batch <= 16 ? 1 : batch <= 32 ? 2 : 4; }
 
+// The column-tile kernel (more than 16 vectors): a workgroup of
+// col_tiles * row_groups waves owns row_groups * row_tiles 16-row tiles;
+// each wave multiplies row_tiles of them by one 16-vector column tile.  Every
+// vector fragment a wave loads serves its row_tiles tiles, so the vectors are
+// read once per 16 * row_tiles * row_groups rows.
+// At 28672 x 8192 the 64-row workgroups took 64 vectors from 107 to 56 us
+// and 32 vectors from 69 to 44 us against 16-row workgroups; 32 rows were
+// slower (75 and 70 us), and for two column tiles one row group of 4 tiles
+// beat two groups of 2 (44 against 50 us).
+#ifndef LOOM_I8_COLS_RT4
+#define LOOM_I8_COLS_RT4 4   // four column tiles: 64 rows per workgroup, one row group
+#endif
+#ifndef LOOM_I8_COLS_RT2
+#define LOOM_I8_COLS_RT2 4   // two column tiles: 64 rows per workgroup, one row group (2 waves)
+#endif
+#ifndef LOOM_I8_COLS_RG2
+#define LOOM_I8_COLS_RG2 1
+#endif
+constexpr int i8_cols_row_tiles(int col_tiles) { return col_tiles == 4 ? LOOM_I8_COLS_RT4 : LOOM_I8_COLS_RT2; }
+constexpr int i8_cols_row_groups(int col_tiles) { return col_tiles == 4 ? 1 : LOOM_I8_COLS_RG2; }
+constexpr int i8_cols_tile_rows(int col_tiles) {
+    return 16 * i8_cols_row_tiles(col_tiles) * i8_cols_row_groups(col_tiles);
+}
+// LDS: two record slots of tile_rows rows x 256 bytes.
+constexpr uint32_t i8_cols_lds_bytes(int col_tiles) { return 2u * 256u * (uint32_t)i8_cols_tile_rows(col_tiles); }
+
 // The row-streaming MFMA kernel: one workgroup of 16 waves per CU (an MI355X
 // has 256) walks 16-row tiles, each wave streaming one whole row per tile
 // into LDS.  It serves batches of 9 to 16 vectors when k is a multiple of

@@ -111,12 +111,14 @@ def test_launch_config_tiles(loom):
     # each) + 4 per-wave 16x256 B weight staging tiles
     assert cfg["workgroup_size"] == (256, 1, 1)
     assert cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096
-    # more than 16 vectors: one wave per 16-vector column tile; LDS: two 16-row x 256 B record slots
+    # more than 16 vectors: 64 rows per workgroup, one wave per 16-vector column
+    # tile (2 or 4); LDS: two 64-row x 256 B record slots
     cfg = loom.launch_config_invoke(i8, [28672, 8192, 64])
-    assert cfg["workgroups"][0] == 1792 and cfg["workgroup_size"] == (256, 1, 1)
-    assert cfg["workgroup_storage_bytes"] == 2 * 4096
+    assert cfg["workgroups"][0] == 448 and cfg["workgroup_size"] == (256, 1, 1)
+    assert cfg["workgroup_storage_bytes"] == 2 * 64 * 256
     cfg = loom.launch_config_invoke(i8, [100, 1000, 17])
-    assert cfg["workgroups"][0] == 7 and cfg["workgroup_size"] == (128, 1, 1)
+    assert cfg["workgroups"][0] == 2 and cfg["workgroup_size"] == (128, 1, 1)
+    assert loom.launch_config_invoke(i8, [5, 64, 33])["workgroups"][0] == 1
     assert loom.launch_config_invoke(i8, [17, 64, 2])["workgroups"][0] == 2
     # 9-16 vectors, k a multiple of 1024 from 4096 to 8192: one 16-wave
     # workgroup per CU walks the 16-row tiles; LDS: the tile (16 rows x k

@@ -281,8 +281,14 @@ I8_CASES = [
     # tiles, so workgroups take two or three tiles each)
     (16, 4096, 9), (17, 4096, 16), (100, 6144, 12), (300, 8192, 16), (47, 5120, 11), (8197, 4096, 16),
     (1000, 7168, 13),
-    # more than 16 vectors: one wave per 16-vector column tile, partial records and tiles
+    # more than 16 vectors: 64-row workgroups, one wave per 16-vector column
+    # tile and row group; partial records, partial tiles, a workgroup with
+    # fewer than 16 rows, exactly one and a few full workgroups
     (33, 8192, 48), (17, 1000, 20), (50, 260, 64), (300, 4096, 40),
+    (5, 2048, 64), (64, 8192, 64), (65, 1024, 33), (192, 2048, 32), (129, 8192, 17),
+    # workgroups start their k walk at different records, wrapping around, also
+    # at a partial last record
+    (200, 1000, 40), (150, 260, 64), (260, 4100, 24),
 ]
 
 
