@@ -392,7 +392,8 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
 
 // ----------------------------------------------------------------------------
 // More than 16 vectors: one workgroup of NT * RG waves owns RG * RT 16-row
-// tiles (64 rows at the default shapes).  Wave (group, c) multiplies the RT
+// tiles (64 rows for two column tiles; for four, the tiles shared evenly
+// between one or two workgroups per CU).  Wave (group, c) multiplies the RT
 // tiles of its row group by the 16-vector column tile c.  The waves split
 // each 256-byte weight record of the workgroup's rows (each loads SHARE
 // instructions of 4 rows x 256 B, whole 256-byte pieces) and store it into
@@ -500,17 +501,33 @@ __global__ __launch_bounds__(kWave * NT * RG) void i8_mfma_cols_kernel(
     }
 }
 
+template <bool FULL, bool VEC16, int RT>
+static void launch_mfma_cols4(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
+                              const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
+                              int32_t *acc) {
+    i8_mfma_cols_kernel<FULL, VEC16, 4, RT, i8_cols_row_groups(4), kI8ColsDepth>
+        <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+}
+
 template <bool FULL, bool VEC16>
 static void launch_mfma_cols(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
                              const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
                              int32_t *acc) {
     // the shapes below are the ones the launch geometry (i8_cols_*) describes
-    if (mfma_col_tiles(batch) == 2)
-        i8_mfma_cols_kernel<FULL, VEC16, 2, i8_cols_row_tiles(2), i8_cols_row_groups(2), kI8ColsDepth>
+    if (mfma_col_tiles(batch) == 2) {
+        i8_mfma_cols_kernel<FULL, VEC16, 2, LOOM_I8_COLS_RT2, i8_cols_row_groups(2), kI8ColsDepth>
             <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
-    else
-        i8_mfma_cols_kernel<FULL, VEC16, 4, i8_cols_row_tiles(4), i8_cols_row_groups(4), kI8ColsDepth>
-            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+        return;
+    }
+    static_assert(kI8ColsMaxRowTiles == 8, "one instantiation per row-tile count");
+    switch (i8_cols_row_tiles(4, rows)) {
+#define LOOM_COLS4_CASE(RT) \
+    case RT: launch_mfma_cols4<FULL, VEC16, RT>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc); break;
+        LOOM_COLS4_CASE(1) LOOM_COLS4_CASE(2) LOOM_COLS4_CASE(3) LOOM_COLS4_CASE(4)
+        LOOM_COLS4_CASE(5) LOOM_COLS4_CASE(6) LOOM_COLS4_CASE(7) LOOM_COLS4_CASE(8)
+#undef LOOM_COLS4_CASE
+        default: break;
+    }
 }
 
 template <int CHUNKS>

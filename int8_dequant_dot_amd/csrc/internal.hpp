@@ -129,26 +129,39 @@ constexpr int mfma_col_tiles(int64_t batch) { return batch <= 16 ? 1 : batch <= 
 // each wave multiplies row_tiles of them by one 16-vector column tile.  Every
 // vector fragment a wave loads serves its row_tiles tiles, so the vectors are
 // read once per 16 * row_tiles * row_groups rows.
-// At 28672 x 8192 the 64-row workgroups took 64 vectors from 107 to 56 us
-// and 32 vectors from 69 to 44 us against 16-row workgroups; 32 rows were
-// slower (75 and 70 us), and for two column tiles one row group of 4 tiles
-// beat two groups of 2 (44 against 50 us).
-#ifndef LOOM_I8_COLS_RT4
-#define LOOM_I8_COLS_RT4 4   // four column tiles: 64 rows per workgroup, one row group
-#endif
+//
+// Two column tiles: one row group of 4 tiles (64 rows, 2 waves).  At 28672 x
+// 8192 x 32 it took 44 us against 69 us with one tile per wave and 50 us with
+// two row groups of 2.
 #ifndef LOOM_I8_COLS_RT2
-#define LOOM_I8_COLS_RT2 4   // two column tiles: 64 rows per workgroup, one row group (2 waves)
+#define LOOM_I8_COLS_RT2 4
 #endif
 #ifndef LOOM_I8_COLS_RG2
 #define LOOM_I8_COLS_RG2 1
 #endif
-constexpr int i8_cols_row_tiles(int col_tiles) { return col_tiles == 4 ? LOOM_I8_COLS_RT4 : LOOM_I8_COLS_RT2; }
+// Four column tiles: the row tiles are shared evenly between q workgroups per
+// CU, q = ceil(tiles / (256 * 8)), so that no CU gets a workgroup more than
+// another (8 row tiles per wave at most).  At 64 vectors and k = 8192, 28672 rows
+// (7 tiles per wave, 256 workgroups) took 48.1 us against 56.0 us with 4 tiles
+// per wave (448 workgroups), 40960 rows (5 tiles, 512 workgroups) 64.3 against
+// 81.1 us, 57344 rows (7 tiles, 512 workgroups) 85.3 against 108.4 us.
+constexpr int kI8ColsMaxRowTiles = 8;
+constexpr int64_t kI8ColsCUs = 256;  // an MI355X has 256 CUs
+constexpr int i8_cols_row_tiles(int col_tiles, int64_t rows) {
+    if (col_tiles != 4) return LOOM_I8_COLS_RT2;
+    const int64_t tiles = (rows + 15) / 16;
+    if (tiles <= 0) return 1;
+    const int64_t per_cu = (tiles + kI8ColsCUs * kI8ColsMaxRowTiles - 1) / (kI8ColsCUs * kI8ColsMaxRowTiles);
+    return (int)((tiles + kI8ColsCUs * per_cu - 1) / (kI8ColsCUs * per_cu));
+}
 constexpr int i8_cols_row_groups(int col_tiles) { return col_tiles == 4 ? 1 : LOOM_I8_COLS_RG2; }
-constexpr int i8_cols_tile_rows(int col_tiles) {
-    return 16 * i8_cols_row_tiles(col_tiles) * i8_cols_row_groups(col_tiles);
+constexpr int i8_cols_tile_rows(int col_tiles, int64_t rows) {
+    return 16 * i8_cols_row_tiles(col_tiles, rows) * i8_cols_row_groups(col_tiles);
 }
 // LDS: two record slots of tile_rows rows x 256 bytes.
-constexpr uint32_t i8_cols_lds_bytes(int col_tiles) { return 2u * 256u * (uint32_t)i8_cols_tile_rows(col_tiles); }
+constexpr uint32_t i8_cols_lds_bytes(int col_tiles, int64_t rows) {
+    return 2u * 256u * (uint32_t)i8_cols_tile_rows(col_tiles, rows);
+}
 
 // The row-streaming MFMA kernel: one workgroup of 16 waves per CU (an MI355X
 // has 256) walks 16-row tiles, each wave streaming one whole row per tile

@@ -92,8 +92,8 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
     }
     if (w[2] > 16) {
         const int nt = mfma_col_tiles(w[2]);
-        return set(c, ceil_div(w[0], i8_cols_tile_rows(nt)), kSubgroupSize * nt * i8_cols_row_groups(nt),
-                   i8_cols_lds_bytes(nt));
+        return set(c, ceil_div(w[0], i8_cols_tile_rows(nt, w[0])), kSubgroupSize * nt * i8_cols_row_groups(nt),
+                   i8_cols_lds_bytes(nt, w[0]));
     }
     return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * kMfmaKSplit,
                (kMfmaKSplit - 1) * 4 * kSubgroupSize * 4 + (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));

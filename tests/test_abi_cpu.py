@@ -111,11 +111,17 @@ def test_launch_config_tiles(loom):
     # each) + 4 per-wave 16x256 B weight staging tiles
     assert cfg["workgroup_size"] == (256, 1, 1)
     assert cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096
-    # more than 16 vectors: 64 rows per workgroup, one wave per 16-vector column
-    # tile (2 or 4); LDS: two 64-row x 256 B record slots
-    cfg = loom.launch_config_invoke(i8, [28672, 8192, 64])
-    assert cfg["workgroups"][0] == 448 and cfg["workgroup_size"] == (256, 1, 1)
-    assert cfg["workgroup_storage_bytes"] == 2 * 64 * 256
+    # more than 16 vectors, four column tiles (33-64): one wave per 16-vector
+    # column tile, the 16-row tiles shared evenly by one or two workgroups per
+    # CU (at most 8 tiles per wave); LDS: two record slots of 256 B per row
+    for rows, rt, groups in ((16384, 4, 256), (28672, 7, 256), (24575, 6, 256), (24576, 6, 256), (4096, 1, 256),
+                             (4097, 2, 129), (32768, 8, 256), (32769, 5, 410), (40960, 5, 512), (57344, 7, 512),
+                             (65536, 8, 512), (65537, 6, 683), (5, 1, 1)):
+        cfg = loom.launch_config_invoke(i8, [rows, 8192, 64])
+        assert cfg["workgroups"][0] == groups == -(-rows // (16 * rt)), rows
+        assert cfg["workgroup_size"] == (256, 1, 1) and cfg["workgroup_storage_bytes"] == 2 * 16 * rt * 256, rows
+    # two column tiles (17-32): 64 rows per workgroup, 2 waves
+    assert loom.launch_config_invoke(i8, [28672, 8192, 32])["workgroups"][0] == 448  # two column tiles: 64 rows
     cfg = loom.launch_config_invoke(i8, [100, 1000, 17])
     assert cfg["workgroups"][0] == 2 and cfg["workgroup_size"] == (128, 1, 1)
     assert loom.launch_config_invoke(i8, [5, 64, 33])["workgroups"][0] == 1

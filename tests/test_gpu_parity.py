@@ -289,6 +289,10 @@ I8_CASES = [
     # workgroups start their k walk at different records, wrapping around, also
     # at a partial last record
     (200, 1000, 40), (150, 260, 64), (260, 4100, 24),
+    # four column tiles: 1 to 8 row tiles per wave (rows shared evenly by one or
+    # two workgroups per CU), the last workgroup partial
+    (5000, 512, 64), (12000, 260, 40), (16384, 256, 33), (20000, 128, 64), (24576, 256, 40),
+    (24600, 1000, 64), (30000, 64, 48), (40000, 64, 64),
 ]
 
 
