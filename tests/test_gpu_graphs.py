@@ -55,6 +55,14 @@ def _cases(loom, dev):
         a = torch.empty(300, batch, dtype=torch.int32, device=dev)
         c[f"i8_dequant_dot_b{batch}"] = (lambda w=w, v=v, ws=ws, vs=vs, y=y, a=a:
                                          loom.i8_dequant_dot(w, ws, v, vs, y, a, want_acc=True))
+    # 64 vectors over 5000 rows: two row tiles per wave in the column-tile kernel
+    wt = loom.pack_int8(synth.i8_rows(6, synth.S_W, 0, 5000, 1024, dev))
+    vt = loom.pack_int8(synth.i8_rows(6, synth.S_X, 0, 64, 1024, dev))
+    wst = synth.scales(6, synth.S_WSCALE, 0, 5000, dev)
+    vst = synth.scales(6, synth.S_XSCALE, 0, 64, dev)
+    yt = torch.empty(5000, 64, device=dev)
+    at = torch.empty(5000, 64, dtype=torch.int32, device=dev)
+    c["i8_dequant_dot_b64_5000"] = lambda: loom.i8_dequant_dot(wt, wst, vt, vst, yt, at, want_acc=True)
     for outputs, records in ((2048, 128), (65536 + 320, 12)):
         f, s, r, i = synth.packed_dot_inputs(records=records, outputs=outputs, device=dev)
         po = torch.empty(outputs, device=dev)
@@ -71,7 +79,7 @@ def _cases(loom, dev):
 
 CASE_NAMES = ["copy_f32", "row_sum_tiles", "row_sums_narrow", "row_sums_tiled", "row_sums_long",
               "segment_sums_256", "segment_sums_300", "i8_dequant_dot_b1", "i8_dequant_dot_b8", "i8_dequant_dot_b16",
-              "i8_dequant_dot_b40",
+              "i8_dequant_dot_b40", "i8_dequant_dot_b64_5000",
               "packed_dot_2048", "packed_dot_65856", "sum_guarded_rows", "routed_combine"]
 
 

@@ -138,6 +138,28 @@ def test_i8_dequant_dot_row_kernel_random_shapes(loom, device):
         assert np.array_equal(_bits(_np(y)), _bits(ry)), what
 
 
+def test_i8_dequant_dot_column_kernel_random_shapes(loom, device):
+    # 17-64 vectors: the column-tile kernel, over row counts that give 1 to 8
+    # row tiles per wave and one or two workgroups per CU, with whole and
+    # partial 256-byte records
+    rng = np.random.default_rng(1011)
+    for case in range(12):
+        rows = int(rng.integers(1, 42000))
+        k = 4 * int(rng.integers(1, 130))
+        batch = int(rng.integers(17, 65))
+        seed = 8000 + case
+        w = synth.i8_rows(seed, synth.S_W, 0, rows, k)
+        x = synth.i8_rows(seed, synth.S_X, 0, batch, k)
+        ws = synth.scales(seed, synth.S_WSCALE, 0, rows)
+        xs = synth.scales(seed, synth.S_XSCALE, 0, batch) if case % 2 else None
+        y, acc = loom.i8_dequant_dot(loom.pack_int8(w.to(device)), ws.to(device), loom.pack_int8(x.to(device)),
+                                     None if xs is None else xs.to(device), want_acc=True)
+        ry, racc = oracle.i8_dequant_dot(w.numpy(), ws.numpy(), x.numpy(), None if xs is None else xs.numpy())
+        what = (case, rows, k, batch)
+        assert np.array_equal(_np(acc), racc), what
+        assert np.array_equal(_bits(_np(y)), _bits(ry)), what
+
+
 def test_packed_dot_random_shapes(loom, device):
     rng = np.random.default_rng(1005)
     shapes = [(int(rng.integers(1, 3000)), int(rng.choice([1, 2, 3, 16, 64, 100])), int(rng.integers(0, 40)))
