@@ -67,6 +67,11 @@ __device__ __forceinline__ int4v load_words(const int32_t *__restrict__ row, int
     return v;
 }
 
+// Row row0 + off, clamped to the last row.  row0 is the first row of a tile
+// that exists (row0 < rows), so neither this nor a store guard of the form
+// off < rows - row0 can overflow, even for rows close to 2^31.
+__device__ __forceinline__ int row_clamped(int row0, int off, int rows) { return row0 + min(off, rows - 1 - row0); }
+
 __device__ __forceinline__ int dot16(int4v a, int4v b, int acc) {
     acc = __builtin_amdgcn_sdot4(a.x, b.x, acc, false);
     acc = __builtin_amdgcn_sdot4(a.y, b.y, acc, false);
@@ -188,13 +193,13 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
     const int m = lane & 15;
     const int g = lane >> 4;
     const int row0 = blockIdx.x * kMfmaTileRows;
-    const int32_t *wrow = w + (int64_t)min(row0 + m, rows - 1) * kw;
+    const int32_t *wrow = w + (int64_t)row_clamped(row0, m, rows) * kw;
     // Staged loads: instruction i of a record reads rows 4i..4i+3 of the tile,
     // 256 contiguous bytes each (lane: row 4i + (lane >> 4), chunk lane & 15).
     const int srow = lane >> 4, schunk = lane & 15;
     const int32_t *wstage[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wstage[i] = w + (int64_t)min(row0 + 4 * i + srow, rows - 1) * kw;
+    for (int i = 0; i < 4; ++i) wstage[i] = w + (int64_t)row_clamped(row0, 4 * i + srow, rows) * kw;
     // Per-wave staging tile: 16 rows x 16 chunks of 16 B; chunk c of row r at
     // slot 16 r + (c ^ r), so both the row-wise writes and the fragment reads
     // (16 rows, one chunk each) fall on distinct banks.
@@ -290,8 +295,8 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
         const float xs = x_scale ? x_scale[n] : 1.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = row0 + 4 * g + i;
-            if (row < rows) {
+            if (4 * g + i < rows - row0) {
+                const int row = row0 + 4 * g + i;
                 const int a = acc[t][i];
                 float y = (float)a;
                 y = y * w_scale[row];
@@ -349,7 +354,7 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
     int4v rowbuf[CHUNKS];
     auto load_row = [&](int t) {
         // rows past the end load the last row; their outputs are never stored
-        const int32_t *src = w + (int64_t)min(t * kMfmaTileRows + wave, rows - 1) * kw;
+        const int32_t *src = w + (int64_t)row_clamped(t * kMfmaTileRows, wave, rows) * kw;
 #pragma unroll
         for (int j = 0; j < CHUNKS; ++j) rowbuf[j] = load_words<true, VEC16, true>(src, (j * kWave + lane) * 4, kw);
     };
@@ -378,8 +383,8 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
             const int r = threadIdx.x >> 4, n = threadIdx.x & 15;
             int sum = 0;
             for (int v = 0; v < kI8RowsWaves; ++v) sum += partial[v][r & 3][(r >> 2) * 16 + n];
-            const int row = t * kMfmaTileRows + r;
-            if (n < batch && row < rows) {
+            if (n < batch && r < rows - t * kMfmaTileRows) {
+                const int row = t * kMfmaTileRows + r;
                 float y = (float)sum;
                 y = y * w_scale[row];
                 if (x_scale) y = y * x_scale[n];
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(kWave * NT * RG) void i8_mfma_cols_kernel(
     const int32_t *wsrc[kShare];
 #pragma unroll
     for (int i = 0; i < kShare; ++i)
-        wsrc[i] = w + (int64_t)min(row0 + (wave * kShare + i) * 4 + srow, rows - 1) * kw;
+        wsrc[i] = w + (int64_t)row_clamped(row0, (wave * kShare + i) * 4 + srow, rows) * kw;
     const int n = ct * 16 + m;  // this lane's vector
     const bool live = n < batch;
     const int32_t *xrow = x + (int64_t)min(n, batch - 1) * kw;
@@ -489,8 +494,9 @@ __global__ __launch_bounds__(kWave * NT * RG) void i8_mfma_cols_kernel(
         for (int j = 0; j < RT; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = row0 + (group * RT + j) * kMfmaTileRows + 4 * g + i;
-                if (row < rows) {
+                const int off = (group * RT + j) * kMfmaTileRows + 4 * g + i;
+                if (off < rows - row0) {
+                    const int row = row0 + off;
                     float y = (float)acc[j][i];
                     y = y * w_scale[row];
                     if (x_scale) y = y * xs;
