@@ -416,8 +416,10 @@ template <int SHARE> struct ColsRecord {
     int4v b[4];        // its vector fragments for the record's 4 k steps
 };
 
+// At least two waves per SIMD (at most 256 registers): two workgroups of
+// four waves share a CU when the rows need two per CU.
 template <bool FULL, bool VEC16, int NT, int RT, int RG, int DEPTH>
-__global__ __launch_bounds__(kWave * NT * RG) void i8_mfma_cols_kernel(
+__global__ __launch_bounds__(kWave * NT * RG, 2) void i8_mfma_cols_kernel(
     const int32_t *__restrict__ w, const float *__restrict__ w_scale, const int32_t *__restrict__ x,
     const float *__restrict__ x_scale, int rows, int kw, int batch, float *__restrict__ out,
     int32_t *__restrict__ acc_out) {

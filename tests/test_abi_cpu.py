@@ -343,6 +343,15 @@ def _kernel_metadata(lib_path, tmp_path):
     return kernels
 
 
+def test_column_kernel_fits_two_workgroups_per_cu(loom, tmp_path):
+    # 33-64 vectors over many rows run two 4-wave workgroups per CU, which
+    # needs at most 256 registers per wave (two waves per SIMD); above that
+    # the second workgroup of each CU waits for the first
+    kernels = [(n, v) for n, _, v in _kernel_metadata(loom.LIB_PATH, tmp_path) if "i8_mfma_cols_kernel" in n]
+    assert kernels
+    assert all(v <= 256 for _, v in kernels), kernels
+
+
 def test_no_kernel_spills_to_scratch(loom, tmp_path):
     # register spills go to per-lane scratch memory, an order of magnitude
     # slower than the streaming loads these kernels are built around
