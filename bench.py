@@ -17,7 +17,8 @@ timed ones never wait for the host).  `cpu_baseline` is
 the CPU oracle on the same workload on one core (also used to check the outputs);
 `cpu_baseline_all_cores` runs the same oracle calls over row blocks on every
 usable host core.  `parts` gives each kernel's mean time and the median and
-minimum of its five per-repetition means; the
+minimum of its five per-repetition means, and the same weights with 64
+vectors (`i8_dequant_dot_batched_64`, outside the step); the
 pages' own launch-bound shapes (the 63x32 tile, the 1009-element copy, the
 guarded 63x32x4 rows, the 2048x128 packed dot, the 256-token routed combines)
 add `us_graph`, the device time per call inside a HIP graph of back-to-back calls.
@@ -239,6 +240,33 @@ def main():
     ops5 = 2 * R5 * K5 * B5
     parts["i8_dequant_dot_batched"]["TOP/s"] = round(ops5 / (per_kernel_ms[2] * 1e-3) / 1e12, 1)
     parts["i8_dequant_dot_batched"]["mfma_util"] = round(ops5 / (per_kernel_ms[2] * 1e-3) / INT8_PEAK_OPS, 4)
+
+    # The same weights with 64 vectors (the column-tile kernel), outside the
+    # step: five repetitions of K back-to-back launches, as above.
+    B6 = 64
+    x6p = loom.pack_int8(synth.i8_matrix(synth.BATCHED.seed, synth.S_X, B6, K5, device=dev))
+    sx6 = synth.scales(synth.BATCHED.seed, synth.S_XSCALE, 0, B6, device=dev)
+    out6 = torch.empty(R5, B6, device=dev)
+    bytes6 = R5 * K5 + B6 * K5 + R5 * 4 + B6 * 4 + R5 * B6 * 4
+    reps6 = []
+    for _ in range(REPS):
+        torch.cuda.synchronize()
+        loom.i8_dequant_dot(w5p[2], s5, x6p, sx6, out=out6)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            loom.i8_dequant_dot(w5p[i % 3], s5, x6p, sx6, out=out6)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps6.append(e0.elapsed_time(e1) / K)
+    ms6 = sum(reps6) / REPS
+    reps6.sort()
+    parts["i8_dequant_dot_batched_64"] = {
+        "bytes": bytes6, "us": round(ms6 * 1e3, 2), "GB/s": round(bytes6 / (ms6 * 1e-3) / 1e9, 1),
+        "frac_of_peak": round(bytes6 / (ms6 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "us_median": round(reps6[REPS // 2] * 1e3, 2), "us_min": round(reps6[0] * 1e3, 2),
+        "TOP/s": round(2 * R5 * K5 * B6 / (ms6 * 1e-3) / 1e12, 1)}
+    del x6p, out6
 
     if args.segments:
         S, CS = 16384, 256

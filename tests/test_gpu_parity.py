@@ -377,6 +377,13 @@ def test_i8_batched_full_size_sampled(loom, device):
     _i8_full(loom, device, synth.BATCHED, 28672, 8192, 8)
 
 
+@pytest.mark.parametrize("rows,k", [(28672, 8192), (57344, 4096)])
+def test_i8_batched_64_full_size_sampled(loom, device, rows, k):
+    # the column-tile kernel at full size: one (7 row tiles per wave) and two
+    # workgroups per CU
+    _i8_full(loom, device, synth.BATCHED, rows, k, 64)
+
+
 def test_tile_workload(loom, device):
     # the pages' own tile: one 63x32 N(0,1) tile, seeded count
     values, count = synth.tile_inputs()
