@@ -11,6 +11,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -341,6 +342,24 @@ def _kernel_metadata(lib_path, tmp_path):
             vgpr = int(re.search(r"\.vgpr_count:\s+(\d+)", entry).group(1))
             kernels.append((name, priv, vgpr))
     return kernels
+
+
+def test_column_kernel_shares_rows_evenly(loom):
+    # 33-64 vectors: for any row count, the 16-row tiles are split into
+    # workgroups of RT tiles (1 <= RT <= 8, read back from the LDS size),
+    # q = ceil(tiles / 2048) workgroups per CU at most, and the last workgroup
+    # still has rows
+    rng = np.random.default_rng(12)
+    i8 = loom.launch_config_lookup("i8_dequant_dot")
+    counts = list(rng.integers(1, 2**31 - 1, 300)) + [1, 16, 17, 4095, 4096, 4097, 32768, 32769, 2**31 - 1]
+    for rows in map(int, counts):
+        cfg = loom.launch_config_invoke(i8, [rows, 64, 64])
+        rt = cfg["workgroup_storage_bytes"] // (2 * 16 * 256)
+        assert cfg["workgroup_storage_bytes"] == rt * 2 * 16 * 256 and 1 <= rt <= 8, rows
+        tiles = -(-rows // 16)
+        groups = cfg["workgroups"][0]
+        assert groups == -(-rows // (16 * rt)) and (groups - 1) * 16 * rt < rows, rows
+        assert groups <= 256 * -(-tiles // 2048), rows
 
 
 def test_column_kernel_fits_two_workgroups_per_cu(loom, tmp_path):
