@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
 // ----------------------------------------------------------------------------
 // More than 16 vectors: one workgroup of NT * RG waves owns RG * RT 16-row
 // tiles (64 rows for two column tiles; for four, the tiles shared evenly
-// between one or two workgroups per CU).  Wave (group, c) multiplies the RT
+// between q workgroups per CU, one or two up to 65536 rows).  Wave (group, c) multiplies the RT
 // tiles of its row group by the 16-vector column tile c.  The waves split
 // each 256-byte weight record of the workgroup's rows (each loads SHARE
 // instructions of 4 rows x 256 B, whole 256-byte pieces) and store it into
@@ -517,24 +517,26 @@ static void launch_mfma_cols4(dim3 grid, dim3 block, hipStream_t stream, const i
         <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
 }
 
+// Returns false, launching nothing, for a row-tile count outside 1..8 (the
+// geometry never produces one).
 template <bool FULL, bool VEC16>
-static void launch_mfma_cols(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
+static bool launch_mfma_cols(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
                              const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
                              int32_t *acc) {
     // the shapes below are the ones the launch geometry (i8_cols_*) describes
     if (mfma_col_tiles(batch) == 2) {
         i8_mfma_cols_kernel<FULL, VEC16, 2, LOOM_I8_COLS_RT2, i8_cols_row_groups(2), kI8ColsDepth>
             <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
-        return;
+        return true;
     }
     static_assert(kI8ColsMaxRowTiles == 8, "one instantiation per row-tile count");
     switch (i8_cols_row_tiles(4, rows)) {
 #define LOOM_COLS4_CASE(RT) \
-    case RT: launch_mfma_cols4<FULL, VEC16, RT>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc); break;
+    case RT: launch_mfma_cols4<FULL, VEC16, RT>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc); return true;
         LOOM_COLS4_CASE(1) LOOM_COLS4_CASE(2) LOOM_COLS4_CASE(3) LOOM_COLS4_CASE(4)
         LOOM_COLS4_CASE(5) LOOM_COLS4_CASE(6) LOOM_COLS4_CASE(7) LOOM_COLS4_CASE(8)
 #undef LOOM_COLS4_CASE
-        default: break;
+        default: return false;
     }
 }
 
@@ -555,15 +557,15 @@ static void launch_mfma_rows(dim3 grid, bool vec16, hipStream_t stream, const in
 }
 
 template <bool FULL, bool VEC16>
-static void launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
+static bool launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
                         const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
                         int32_t *acc) {
     constexpr bool kStage = kMfmaStage;
     if (batch > 16)
-        launch_mfma_cols<FULL, VEC16>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc);
-    else
-        i8_mfma_kernel<FULL, VEC16, kStage, kMfmaDepth, kMfmaSteps, 1>
-            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+        return launch_mfma_cols<FULL, VEC16>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+    i8_mfma_kernel<FULL, VEC16, kStage, kMfmaDepth, kMfmaSteps, 1>
+        <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
+    return true;
 }
 
 hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,
@@ -600,12 +602,16 @@ hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w
                                                                                        k_words, rpw, out, acc);
     } else {
         const bool full = k_words % (16 * kMfmaSteps) == 0;
+        bool launched;
         if (full && vec16)
-            launch_mfma<true, true>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc);
+            launched = launch_mfma<true, true>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc);
         else if (vec16)
-            launch_mfma<false, true>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc);
+            launched = launch_mfma<false, true>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out,
+                                                acc);
         else
-            launch_mfma<false, false>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc);
+            launched = launch_mfma<false, false>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, batch, out,
+                                                 acc);
+        if (!launched) return hipErrorInvalidConfiguration;
     }
     return hipGetLastError();
 }
