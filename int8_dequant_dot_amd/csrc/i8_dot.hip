@@ -158,9 +158,9 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
 // ----------------------------------------------------------------------------
 // Several vectors (batch >= 2): the shared activations make this a dense
 // int8 contraction, so it runs on the matrix cores.  One workgroup owns a
-// 16-row tile; its kMfmaKSplit waves each take a contiguous quarter of k (of
-// the records), and their int32 partial tiles are added in wave order at the
-// end (exact).  Each k step is one v_mfma_i32_16x16x64_i8:
+// 16-row tile; its KS waves (1, 2, 4 or 8: about 2 KiB of every row per wave,
+// mfma_ksplit) each take a contiguous share of k (of the records), and their
+// int32 partial tiles are added in wave order at the end (exact).  Each k step is one v_mfma_i32_16x16x64_i8:
 //   A (16 x 64, weights):  lane l holds 16 bytes of row (l & 15) at byte
 //                          offset 16*(l >> 4) of the 64-byte step;
 //   B (64 x 16, vectors):  lane l holds the same 16 byte positions of vector
@@ -182,8 +182,8 @@ struct MfmaRecord {
     int4v b[NT][S];
 };
 
-template <bool FULL, bool VEC16, bool STAGE, int DEPTH, int S, int NT>
-__global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
+template <bool FULL, bool VEC16, bool STAGE, int DEPTH, int S, int NT, int KS>
+__global__ __launch_bounds__(kWave * KS) void i8_mfma_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
                                                         const int32_t *__restrict__ x,
                                                         const float *__restrict__ x_scale, int rows, int kw, int batch,
                                                         float *__restrict__ out, int32_t *__restrict__ acc_out) {
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
     // Per-wave staging tile: 16 rows x 16 chunks of 16 B; chunk c of row r at
     // slot 16 r + (c ^ r), so both the row-wise writes and the fragment reads
     // (16 rows, one chunk each) fall on distinct banks.
-    __shared__ int4v stage[STAGE ? kMfmaKSplit : 1][STAGE ? 16 * 16 : 1];
+    __shared__ int4v stage[STAGE ? KS : 1][STAGE ? 16 * 16 : 1];
     const int32_t *xrow[NT];
     bool xlive[NT];
 #pragma unroll
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     // this wave's contiguous share of the k records
     const int all_records = (steps + S - 1) / S;
-    const int per_wave = (all_records + kMfmaKSplit - 1) / kMfmaKSplit;
+    const int per_wave = (all_records + KS - 1) / KS;
     const int first = min(all_records, wave * per_wave);
     const int records = min(all_records, first + per_wave) - first;
 
@@ -270,9 +270,9 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
             }
         });
 
-    if constexpr (kMfmaKSplit > 1) {
+    if constexpr (KS > 1) {
         // waves 1.. publish their partial tiles; wave 0 adds them in wave order
-        __shared__ int partial[kMfmaKSplit > 1 ? kMfmaKSplit - 1 : 1][NT][4][kWave];
+        __shared__ int partial[KS > 1 ? KS - 1 : 1][NT][4][kWave];
         if (wave > 0) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kWave * kMfmaKSplit) void i8_mfma_kernel(const int3
         }
         __syncthreads();
         if (wave != 0) return;
-        for (int v = 0; v < kMfmaKSplit - 1; ++v)
+        for (int v = 0; v < KS - 1; ++v)
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -563,9 +563,17 @@ static bool launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t
     constexpr bool kStage = kMfmaStage;
     if (batch > 16)
         return launch_mfma_cols<FULL, VEC16>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc);
-    i8_mfma_kernel<FULL, VEC16, kStage, kMfmaDepth, kMfmaSteps, 1>
-        <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
-    return true;
+    // the split is the one the launch geometry (mfma_ksplit) describes
+    switch (mfma_ksplit(4 * (int64_t)kw, rows)) {
+#define LOOM_MFMA_CASE(KS)                                                                                    \
+    case KS:                                                                                                  \
+        i8_mfma_kernel<FULL, VEC16, kStage, kMfmaDepth, kMfmaSteps, 1, KS>                                    \
+            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);                  \
+        return true;
+        LOOM_MFMA_CASE(1) LOOM_MFMA_CASE(2) LOOM_MFMA_CASE(4) LOOM_MFMA_CASE(8)
+#undef LOOM_MFMA_CASE
+        default: return false;
+    }
 }
 
 hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,

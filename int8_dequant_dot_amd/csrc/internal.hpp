@@ -88,14 +88,22 @@ constexpr int gemv_rows_per_wave(int64_t k_words) {
     const int64_t r = k_words > 0 ? LOOM_GEMV_WAVE_BYTES / (4 * k_words) : 64;
     return r < 1 ? 1 : r > 64 ? 64 : (int)r;
 }
-#ifndef LOOM_MFMA_KSPLIT
-#define LOOM_MFMA_KSPLIT 4    // 4 waves per 16-row tile: 7168 waves for 28672 rows
-#endif
+// Waves per 16-row tile of the tile kernel, each taking a contiguous 1/KS of
+// k: about 2 KiB of every row per wave.  Over ~224 MiB of weights with 2 and
+// 8 vectors, the best split was 1 wave up to k = 2048 (k = 512: 41-47 us
+// against 69-72 with 4 waves), 2 at k = 4096, 4 at k = 8192 and 8 at
+// k = 16384 (41-44 against 44-47 us); with fewer than 512 tiles, 8-wave
+// workgroups leave CUs unevenly loaded (k = 32768, 7168 rows: 57 against 42 us
+// with 4).
+constexpr int mfma_ksplit(int64_t k, int64_t rows) {
+    const int64_t tiles = (rows + 15) / 16;
+    if (k >= 16384 && tiles >= 512) return 8;
+    return k >= 8192 ? 4 : k >= 4096 ? 2 : 1;
+}
 #ifndef LOOM_MFMA_STAGE
 #define LOOM_MFMA_STAGE 1     // weights reach the MFMA through a per-wave LDS tile
 #endif
 constexpr int kMfmaTileRows = 16;
-constexpr int kMfmaKSplit = LOOM_MFMA_KSPLIT;
 constexpr bool kMfmaStage = LOOM_MFMA_STAGE != 0;
 constexpr uint32_t kMfmaStageBytes = 16 * 256;  // per wave: 16 rows x 256 B
 // Outputs per lane of the packed-dot recurrence: kPackedDotWide, spaced one

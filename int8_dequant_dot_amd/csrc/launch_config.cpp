@@ -80,8 +80,8 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 // tile) that walks the tiles; for more than 16 vectors, one workgroup per
 // i8_cols_tile_rows rows with one wave per 16-vector column tile and row group
 // (LDS: two record slots of 256 bytes per row); otherwise one workgroup per
-// 16-row matrix-core tile whose KSPLIT waves split k (the LDS holds their
-// partial accumulators and the weight staging tiles).
+// 16-row matrix-core tile whose mfma_ksplit(k, rows) waves split k (the LDS
+// holds their partial accumulators and the weight staging tiles).
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
     if (w[2] == 1) return set(c, ceil_div(w[0], gemv_rows_per_wave(w[1] / 4)), kSubgroupSize, 0);
@@ -95,8 +95,9 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
         return set(c, ceil_div(w[0], i8_cols_tile_rows(nt, w[0])), kSubgroupSize * nt * i8_cols_row_groups(nt),
                    i8_cols_lds_bytes(nt, w[0]));
     }
-    return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * kMfmaKSplit,
-               (kMfmaKSplit - 1) * 4 * kSubgroupSize * 4 + (kMfmaStage ? kMfmaKSplit * kMfmaStageBytes : 0));
+    const int ks = mfma_ksplit(w[1], w[0]);
+    return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * ks,
+               (ks - 1) * 4 * kSubgroupSize * 4 + (kMfmaStage ? ks * kMfmaStageBytes : 0));
 }
 
 // packed_dot(outputs, count, streams): 256 lanes per workgroup, one output

@@ -135,9 +135,18 @@ def test_launch_config_tiles(loom):
     assert cfg["workgroup_storage_bytes"] == 16 * 8192 + 16 * 1024
     assert loom.launch_config_invoke(i8, [100, 5120, 9])["workgroups"][0] == 7
     assert loom.launch_config_invoke(i8, [100, 5120, 9])["workgroup_storage_bytes"] == 16 * 5120 + 16 * 1024
-    for shape in ([28672, 8192, 8], [100, 1000, 12], [100, 9216, 12], [15, 4096, 12], [100, 3072, 16]):
-        cfg = loom.launch_config_invoke(i8, shape)  # the tile-per-workgroup kernel
-        assert cfg["workgroup_size"] == (256, 1, 1) and cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096, shape
+    # the tile-per-workgroup kernel: about 2 KiB of every row per wave, so 1
+    # wave per tile up to k = 2048, 2 at 4096, 4 from 8192, and 8 from 16384
+    # when there are at least 512 tiles; LDS: (waves - 1) int32 partial tiles
+    # of 1 KiB and one 16 x 256 B staging tile per wave
+    for shape, ks in (([28672, 8192, 8], 4), ([100, 1000, 12], 1), ([100, 9216, 12], 4), ([15, 4096, 12], 2),
+                      ([100, 3072, 16], 1), ([229376, 1024, 8], 1), ([114688, 2048, 2], 1), ([57344, 4096, 8], 2),
+                      ([14336, 16384, 8], 8), ([8192, 16384, 8], 8), ([8176, 16384, 8], 4), ([7168, 32768, 2], 4),
+                      ([5, 65536, 2], 4), ([100, 4, 2], 1), ([100, 0, 2], 1)):
+        cfg = loom.launch_config_invoke(i8, shape)
+        assert cfg["workgroups"][0] == -(-shape[0] // 16), shape
+        assert cfg["workgroup_size"] == (64 * ks, 1, 1), shape
+        assert cfg["workgroup_storage_bytes"] == (ks - 1) * 1024 + ks * 4096, shape
     t = loom.launch_config_lookup("row_sum_tiles")
     assert loom.launch_config_invoke(t, [63])["workgroups"] == (1, 1, 1)
     assert loom.launch_config_invoke(t, [63])["workgroup_size"] == (64, 1, 1)

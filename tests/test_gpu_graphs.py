@@ -55,6 +55,13 @@ def _cases(loom, dev):
         a = torch.empty(300, batch, dtype=torch.int32, device=dev)
         c[f"i8_dequant_dot_b{batch}"] = (lambda w=w, v=v, ws=ws, vs=vs, y=y, a=a:
                                          loom.i8_dequant_dot(w, ws, v, vs, y, a, want_acc=True))
+    # 4 vectors at k = 1024: one wave per 16-row tile
+    wk = loom.pack_int8(synth.i8_rows(7, synth.S_W, 0, 300, 1024, dev))
+    vk = loom.pack_int8(synth.i8_rows(7, synth.S_X, 0, 4, 1024, dev))
+    wsk = synth.scales(7, synth.S_WSCALE, 0, 300, dev)
+    yk = torch.empty(300, 4, device=dev)
+    ak = torch.empty(300, 4, dtype=torch.int32, device=dev)
+    c["i8_dequant_dot_b4_k1024"] = lambda: loom.i8_dequant_dot(wk, wsk, vk, None, yk, ak, want_acc=True)
     # 64 vectors over 5000 rows: two row tiles per wave in the column-tile kernel
     wt = loom.pack_int8(synth.i8_rows(6, synth.S_W, 0, 5000, 1024, dev))
     vt = loom.pack_int8(synth.i8_rows(6, synth.S_X, 0, 64, 1024, dev))
@@ -79,7 +86,7 @@ def _cases(loom, dev):
 
 CASE_NAMES = ["copy_f32", "row_sum_tiles", "row_sums_narrow", "row_sums_tiled", "row_sums_long",
               "segment_sums_256", "segment_sums_300", "i8_dequant_dot_b1", "i8_dequant_dot_b8", "i8_dequant_dot_b16",
-              "i8_dequant_dot_b40", "i8_dequant_dot_b64_5000",
+              "i8_dequant_dot_b40", "i8_dequant_dot_b64_5000", "i8_dequant_dot_b4_k1024",
               "packed_dot_2048", "packed_dot_65856", "sum_guarded_rows", "routed_combine"]
 
 

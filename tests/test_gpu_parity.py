@@ -276,6 +276,10 @@ I8_CASES = [
     (1, 4, 1), (7, 4, 1), (8, 1024, 1), (9, 1028, 1), (17, 8192, 1), (33, 1040, 1), (100, 2112, 1), (5, 0, 1),
     (3, 64, 2), (15, 256, 3), (16, 260, 8), (17, 1000, 8), (100, 8192, 8), (33, 64, 16), (40, 512, 17),
     (20, 1024, 32), (18, 320, 33), (16, 4096, 64), (1, 4, 2), (31, 8, 5),
+    # the tile kernel's k split: 1 wave per tile (k <= 2048, several records),
+    # 2 (k = 4096), 4 (k = 16384 with few tiles, k = 32768) and 8 (k = 16384,
+    # 513 tiles)
+    (1000, 2048, 7), (100, 4096, 8), (300, 16384, 8), (50, 32768, 2), (8200, 16384, 3),
     # 9-16 vectors with k a multiple of 1024 from 4096 to 8192: the row-streaming
     # kernel (one workgroup per CU walking 16-row tiles; 8197 rows give 513
     # tiles, so workgroups take two or three tiles each)
