@@ -179,8 +179,9 @@ int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets
  *     acc[r][b] = sum_{i < k} w[r][i] * x[b][i]          (exact, int32)     *
  *     out[r][b] = (f32(acc[r][b]) * w_scale[r]) * x_scale[b]                *
  * with each product rounded once to f32; when x_scale is NULL the second    *
- * product is skipped.  batch == 1 runs a v_dot4 (int8x4) GEMV; batch >= 2   *
- * runs an int8 MFMA kernel.                                                 *
+ * product is skipped.  One vector with k a multiple of 1024 or k >= 12288  *
+ * runs a v_dot4 (int8x4) GEMV; every other call an int8 MFMA kernel.  The   *
+ * results are the same bits either way.                                     *
  *   w       : int32[rows][k/4] packed int8 weights, device, 4-byte aligned  *
  *   w_scale : f32[rows], device                                             *
  *   x       : int32[batch][k/4] packed int8 activations, device             *

@@ -593,7 +593,7 @@ hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w
         case 8: launch_mfma_rows<8>(grid, vec16, stream, w, w_scale, x, x_scale, rows, k_words, batch, out, acc); return hipGetLastError();
         default: break;
     }
-    if (batch == 1) {
+    if (i8_use_gemv(4 * (int64_t)k_words, batch)) {
         const bool full = k_words % (kWave * 4) == 0;
         const int rpw = gemv_rows_per_wave(k_words);
         if (full && vec16 && rpw == 1)

@@ -84,6 +84,23 @@ constexpr int kSegmentBlockCols = 256;
 #ifndef LOOM_GEMV_WAVE_BYTES
 #define LOOM_GEMV_WAVE_BYTES 8192  // 1 row per wave at k = 8192: 6% faster than 4-row tiles
 #endif
+// One vector runs the GEMV when its rows are whole 1 KiB records (k a
+// multiple of 1024) or long (k >= LOOM_GEMV_ANY_K); other rows go to the
+// matrix-core tile kernel.  The GEMV reduces across the whole wave once per
+// row, and a row's last record is partly empty when k is not a multiple of
+// 1024.  Over 128 MiB of weights, the tile kernel took k = 512 from 76.3 to
+// 24.8 us, 1280 from 40.9 to 23.6, 2560 from 28.1 to 24.4; the GEMV kept
+// k = 1024 (20.9 against 23.5), 8192 (21.1 against 22.6) and 12800 (23.1
+// against 25.0).
+#ifndef LOOM_GEMV_MIN_K
+#define LOOM_GEMV_MIN_K 1024
+#endif
+#ifndef LOOM_GEMV_ANY_K
+#define LOOM_GEMV_ANY_K 12288
+#endif
+constexpr bool i8_use_gemv(int64_t k, int64_t batch) {
+    return batch == 1 && k >= LOOM_GEMV_MIN_K && (k % 1024 == 0 || k >= LOOM_GEMV_ANY_K);
+}
 constexpr int gemv_rows_per_wave(int64_t k_words) {
     const int64_t r = k_words > 0 ? LOOM_GEMV_WAVE_BYTES / (4 * k_words) : 64;
     return r < 1 ? 1 : r > 64 ? 64 : (int)r;

@@ -74,8 +74,8 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
     return set2(c, w[0], blocks, kSubgroupSize, 0);
 }
 
-// i8_dequant_dot(rows, k, batch): for one vector, one wave per block of
-// gemv_rows_per_wave(k) rows; for 9 to 16 vectors and k a multiple of 1024
+// i8_dequant_dot(rows, k, batch): for one vector and k that i8_use_gemv
+// admits, one wave per block of gemv_rows_per_wave(k) rows; for 9 to 16 vectors and k a multiple of 1024
 // from 4096 to 8192, one 16-wave workgroup per CU (at most one per 16-row
 // tile) that walks the tiles; for more than 16 vectors, one workgroup per
 // i8_cols_tile_rows rows with one wave per 16-vector column tile and row group
@@ -84,7 +84,7 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 // holds their partial accumulators and the weight staging tiles).
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
-    if (w[2] == 1) return set(c, ceil_div(w[0], gemv_rows_per_wave(w[1] / 4)), kSubgroupSize, 0);
+    if (i8_use_gemv(w[1], w[2])) return set(c, ceil_div(w[0], gemv_rows_per_wave(w[1] / 4)), kSubgroupSize, 0);
     if (const int chunks = i8_rows_chunks(w[0], w[1], w[2])) {
         const int64_t tiles = ceil_div(w[0], kMfmaTileRows);
         return set(c, tiles < kI8RowsGroups ? tiles : kI8RowsGroups, kSubgroupSize * kI8RowsWaves,

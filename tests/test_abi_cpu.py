@@ -106,6 +106,14 @@ def test_launch_config_tiles(loom):
     assert loom.launch_config_invoke(seg, [5, 0])["workgroups"] == (5, 1, 1)  # still writes the tail counts
     i8 = loom.launch_config_lookup("i8_dequant_dot")
     assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 16384  # one 8 KiB row per wave
+    # one vector: the GEMV for whole 1 KiB records or k >= 12288, else the
+    # matrix-core tile kernel (one wave per 16-row tile below k = 4096)
+    assert loom.launch_config_invoke(i8, [100, 1024, 1])["workgroups"] == (13, 1, 1)  # 8 rows per wave
+    assert loom.launch_config_invoke(i8, [100, 12804, 1])["workgroups"] == (100, 1, 1)
+    for k in (0, 4, 512, 1028, 1536, 2560, 8704):
+        cfg = loom.launch_config_invoke(i8, [100, k, 1])
+        assert cfg["workgroups"] == (7, 1, 1) and cfg["workgroup_size"][0] == 64 * (2 if k >= 4096 else 1) * (
+            2 if k >= 8192 else 1), k
     cfg = loom.launch_config_invoke(i8, [28672, 8192, 8])
     assert cfg["workgroups"][0] == 1792
     # 4 waves split k per 16-row tile; LDS: 3 waves' int32 partial tiles (1 KiB

@@ -273,7 +273,10 @@ def _check_i8(gy, gacc, w, x, ws, xs, what):
 
 I8_CASES = [
     # (rows, k, batch) -- batch 1 runs v_dot4, batch >= 2 the MFMA kernel
+    # (one vector with k a multiple of 1024 or k >= 12288 runs the GEMV, any
+    # other k the matrix-core tile kernel)
     (1, 4, 1), (7, 4, 1), (8, 1024, 1), (9, 1028, 1), (17, 8192, 1), (33, 1040, 1), (100, 2112, 1), (5, 0, 1),
+    (3000, 1536, 1), (40, 12804, 1), (70, 3072, 1),
     (3, 64, 2), (15, 256, 3), (16, 260, 8), (17, 1000, 8), (100, 8192, 8), (33, 64, 16), (40, 512, 17),
     (20, 1024, 32), (18, 320, 33), (16, 4096, 64), (1, 4, 2), (31, 8, 5),
     # the tile kernel's k split: 1 wave per tile (k <= 2048, several records),
