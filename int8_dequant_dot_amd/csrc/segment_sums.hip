@@ -68,10 +68,41 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
     }
 }
 
+// Rows in flight per wave.  A launch of many waves (segments x 256-column
+// blocks) keeps HBM busy with 8 rows each (7 KiB per wave at 256 columns);
+// with few waves each needs a deeper ring.  Over ~1-4 GB: 16384 segments
+// (depth 8 / 16) 677.7 / 693.6 us; 2048 waves 734.9 / 735.3 / 721.0 us at
+// depth 8 / 16 / 32; 1024 waves (128 columns) 290.7 / 221.7; 512 waves 276.3
+// / 195.0 / 198.6; 128 waves 912.4 / 525.4 / 336.6 us.  The order of every
+// column's sum is the same at any depth.
 #ifndef LOOM_SEGMENT_SUMS_DEPTH
-#define LOOM_SEGMENT_SUMS_DEPTH 8  // 7 rows (7 KiB per wave at 256 columns) in flight
+#define LOOM_SEGMENT_SUMS_DEPTH 8
 #endif
 constexpr int kSegmentDepth = LOOM_SEGMENT_SUMS_DEPTH;
+constexpr int segment_sums_depth(int64_t waves) {
+    return waves <= 256 ? 4 * kSegmentDepth : waves <= 1024 ? 2 * kSegmentDepth : kSegmentDepth;
+}
+
+template <int DEPTH>
+static void launch_segment_sums_depth(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
+                                      const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
+                                      hipStream_t stream) {
+    if (vec4) {
+        if (cols % (kWave * 4) == 0)
+            segment_sums_kernel<4, true, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out,
+                                                                            tail_counts);
+        else
+            segment_sums_kernel<4, false, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out,
+                                                                             tail_counts);
+    } else {
+        if (cols % kWave == 0)
+            segment_sums_kernel<1, true, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out,
+                                                                            tail_counts);
+        else
+            segment_sums_kernel<1, false, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out,
+                                                                             tail_counts);
+    }
+}
 
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
                                const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
@@ -79,20 +110,19 @@ hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, in
     const dim3 grid(cfg.workgroups[0], cfg.workgroups[1]), block(cfg.workgroup_size[0]);
     const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0) &&
                       (cols % 4 == 0);
-    if (vec4) {
-        if (cols % (kWave * 4) == 0)
-            segment_sums_kernel<4, true, kSegmentDepth>
-                <<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out, tail_counts);
-        else
-            segment_sums_kernel<4, false, kSegmentDepth>
-                <<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out, tail_counts);
-    } else {
-        if (cols % kWave == 0)
-            segment_sums_kernel<1, true, kSegmentDepth>
-                <<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out, tail_counts);
-        else
-            segment_sums_kernel<1, false, kSegmentDepth>
-                <<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out, tail_counts);
+    switch (segment_sums_depth((int64_t)cfg.workgroups[0] * cfg.workgroups[1])) {
+        case 4 * kSegmentDepth:
+            launch_segment_sums_depth<4 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, cols, out,
+                                                         tail_counts, stream);
+            break;
+        case 2 * kSegmentDepth:
+            launch_segment_sums_depth<2 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, cols, out,
+                                                         tail_counts, stream);
+            break;
+        default:
+            launch_segment_sums_depth<kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, cols, out,
+                                                     tail_counts, stream);
+            break;
     }
     return hipGetLastError();
 }

@@ -198,6 +198,21 @@ def test_segment_sums_exact(loom, device, lengths, cols):
     assert np.array_equal(_np(tails), rtails)
 
 
+@pytest.mark.parametrize("segments,max_len,cols", [(200, 3000, 256), (600, 200, 256), (250, 300, 1000),
+                                                     (1100, 50, 256), (300, 64, 1000)])
+def test_segment_sums_ring_depths(loom, device, segments, max_len, cols):
+    # the read-ahead depth follows the wave count (segments x 256-column
+    # blocks): 32 rows up to 256 waves, 16 up to 1024, 8 above; every depth
+    # gives the same bits
+    L = synth.segment_lengths(77, segments, max_len)
+    off = synth.segment_offsets(L)
+    x = synth.segment_rows(synth.SEGMENTS.seed, 0, int(off[-1]), cols)
+    out, tails = loom.segment_sums(x.to(device), off.to(device))
+    ref, rtails, _, _ = oracle.segment_sums(x.numpy(), off.numpy())
+    assert np.array_equal(_np(out).view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(_np(tails), rtails)
+
+
 def test_segment_sums_page_vectors(loom, device):
     # the pages' printed column sums of the 64x32 iota, as one segment each
     from tests.golden import load as golden
