@@ -396,20 +396,21 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// More than 16 vectors: one workgroup of NT * RG waves owns RG * RT 16-row
-// tiles (64 rows for two column tiles; for four, the tiles shared evenly
-// between q workgroups per CU, one or two up to 65536 rows).  Wave (group, c) multiplies the RT
-// tiles of its row group by the 16-vector column tile c.  The waves split
-// each 256-byte weight record of the workgroup's rows (each loads SHARE
-// instructions of 4 rows x 256 B, whole 256-byte pieces) and store it into
-// one of two LDS slots, swizzled as in the kernels above; after a barrier
-// each wave multiplies its RT tiles of the record by its own vector
+// More than 16 vectors: one workgroup of 4 waves, one per 16-vector column
+// tile (columns past the batch are zeroed), owns RT 16-row tiles, the tiles
+// shared evenly between q workgroups per CU (one or two up to 65536 rows).
+// The waves split each 256-byte weight record of the workgroup's rows (each
+// loads SHARE instructions of 4 rows x 256 B, whole 256-byte pieces) and
+// store it into one of two LDS slots, swizzled as in the kernels above; after
+// a barrier each wave multiplies all RT tiles of the record by its own vector
 // fragments (4 k steps), which it loads once per record for all RT tiles, so
-// the vectors are read from the caches once per RT * RG tiles instead of
-// once per tile.  Every wave covers the full k for its outputs and stores them
+// the vectors are read from the caches once per RT tiles instead of once per
+// tile.  Every wave covers the full k for its outputs and stores them
 // directly.  A barrier per record is enough with two slots: a wave can only
 // overwrite a slot after every wave has passed the next record's barrier,
-// that is, after all of them have finished reading it.
+// that is, after all of them have finished reading it.  (The template also
+// takes 2 column tiles and RG row groups of RT tiles each; the library
+// launches 4 column tiles and one row group.)
 // ----------------------------------------------------------------------------
 template <int SHARE> struct ColsRecord {
     int4v a[SHARE];    // this wave's share of the record: SHARE loads of 4 rows x 256 B
@@ -513,7 +514,7 @@ template <bool FULL, bool VEC16, int RT>
 static void launch_mfma_cols4(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
                               const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
                               int32_t *acc) {
-    i8_mfma_cols_kernel<FULL, VEC16, 4, RT, i8_cols_row_groups(4), kI8ColsDepth>
+    i8_mfma_cols_kernel<FULL, VEC16, 4, RT, 1, kI8ColsDepth>
         <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
 }
 
@@ -524,13 +525,8 @@ static bool launch_mfma_cols(dim3 grid, dim3 block, hipStream_t stream, const in
                              const int32_t *x, const float *x_scale, int rows, int kw, int batch, float *out,
                              int32_t *acc) {
     // the shapes below are the ones the launch geometry (i8_cols_*) describes
-    if (mfma_col_tiles(batch) == 2) {
-        i8_mfma_cols_kernel<FULL, VEC16, 2, LOOM_I8_COLS_RT2, i8_cols_row_groups(2), kI8ColsDepth>
-            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);
-        return true;
-    }
     static_assert(kI8ColsMaxRowTiles == 8, "one instantiation per row-tile count");
-    switch (i8_cols_row_tiles(4, rows)) {
+    switch (i8_cols_row_tiles(rows)) {
 #define LOOM_COLS4_CASE(RT) \
     case RT: launch_mfma_cols4<FULL, VEC16, RT>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc); return true;
         LOOM_COLS4_CASE(1) LOOM_COLS4_CASE(2) LOOM_COLS4_CASE(3) LOOM_COLS4_CASE(4)

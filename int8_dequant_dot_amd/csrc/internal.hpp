@@ -146,47 +146,32 @@ constexpr int packed_dot_outputs_per_lane(int64_t outputs, int64_t streams) {
 #endif
 constexpr int kRoutedColumnsPerWave = LOOM_ROUTED_COLUMNS;
 
-// 16-vector column tiles the MFMA kernel needs for a batch.
-constexpr int mfma_col_tiles(int64_t batch) { return batch <= 16 ? 1 : batch <= 32 ? 2 : 4; }
+// 16-vector column tiles the MFMA kernels use for a batch: one up to 16
+// vectors, else four (17-32 vectors leave some zeroed: at 28672 x 8192 x 32
+// the four-tile kernel took 40.3 us against 44.1 us with two tiles of 64-row
+// workgroups).
+constexpr int mfma_col_tiles(int64_t batch) { return batch <= 16 ? 1 : 4; }
 
-// The column-tile kernel (more than 16 vectors): a workgroup of
-// col_tiles * row_groups waves owns row_groups * row_tiles 16-row tiles;
-// each wave multiplies row_tiles of them by one 16-vector column tile.  Every
-// vector fragment a wave loads serves its row_tiles tiles, so the vectors are
-// read once per 16 * row_tiles * row_groups rows.
-//
-// Two column tiles: one row group of 4 tiles (64 rows, 2 waves).  At 28672 x
-// 8192 x 32 it took 44 us against 69 us with one tile per wave and 50 us with
-// two row groups of 2.
-#ifndef LOOM_I8_COLS_RT2
-#define LOOM_I8_COLS_RT2 4
-#endif
-#ifndef LOOM_I8_COLS_RG2
-#define LOOM_I8_COLS_RG2 1
-#endif
-// Four column tiles: the row tiles are shared evenly between q workgroups per
+// The column-tile kernel (more than 16 vectors): a workgroup of 4 waves, one
+// per 16-vector column tile, owns row_tiles 16-row tiles; each wave multiplies
+// all of them by its column tile, so every vector fragment it loads serves
+// row_tiles tiles.  The row tiles are shared evenly between q workgroups per
 // CU, q = ceil(tiles / (256 * 8)), so that no CU gets a workgroup more than
-// another (8 row tiles per wave at most).  At 64 vectors and k = 8192, 28672 rows
-// (7 tiles per wave, 256 workgroups) took 48.1 us against 56.0 us with 4 tiles
-// per wave (448 workgroups), 40960 rows (5 tiles, 512 workgroups) 64.3 against
-// 81.1 us, 57344 rows (7 tiles, 512 workgroups) 85.3 against 108.4 us.
+// another (8 row tiles per wave at most).  At 64 vectors and k = 8192, 28672
+// rows (7 tiles per wave, 256 workgroups) took 48.1 us against 56.0 us with 4
+// tiles per wave (448 workgroups), 40960 rows (5 tiles, 512 workgroups) 64.3
+// against 81.1 us, 57344 rows (7 tiles, 512 workgroups) 85.3 against 108.4 us.
 constexpr int kI8ColsMaxRowTiles = 8;
 constexpr int64_t kI8ColsCUs = 256;  // an MI355X has 256 CUs
-constexpr int i8_cols_row_tiles(int col_tiles, int64_t rows) {
-    if (col_tiles != 4) return LOOM_I8_COLS_RT2;
+constexpr int i8_cols_row_tiles(int64_t rows) {
     const int64_t tiles = (rows + 15) / 16;
     if (tiles <= 0) return 1;
     const int64_t per_cu = (tiles + kI8ColsCUs * kI8ColsMaxRowTiles - 1) / (kI8ColsCUs * kI8ColsMaxRowTiles);
     return (int)((tiles + kI8ColsCUs * per_cu - 1) / (kI8ColsCUs * per_cu));
 }
-constexpr int i8_cols_row_groups(int col_tiles) { return col_tiles == 4 ? 1 : LOOM_I8_COLS_RG2; }
-constexpr int i8_cols_tile_rows(int col_tiles, int64_t rows) {
-    return 16 * i8_cols_row_tiles(col_tiles, rows) * i8_cols_row_groups(col_tiles);
-}
+constexpr int i8_cols_tile_rows(int64_t rows) { return 16 * i8_cols_row_tiles(rows); }
 // LDS: two record slots of tile_rows rows x 256 bytes.
-constexpr uint32_t i8_cols_lds_bytes(int col_tiles, int64_t rows) {
-    return 2u * 256u * (uint32_t)i8_cols_tile_rows(col_tiles, rows);
-}
+constexpr uint32_t i8_cols_lds_bytes(int64_t rows) { return 2u * 256u * (uint32_t)i8_cols_tile_rows(rows); }
 
 // The row-streaming MFMA kernel: one workgroup of 16 waves per CU (an MI355X
 // has 256) walks 16-row tiles, each wave streaming one whole row per tile

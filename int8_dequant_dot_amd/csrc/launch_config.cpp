@@ -78,8 +78,8 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 // admits, one wave per block of gemv_rows_per_wave(k) rows; for 9 to 16 vectors and k a multiple of 1024
 // from 4096 to 8192, one 16-wave workgroup per CU (at most one per 16-row
 // tile) that walks the tiles; for more than 16 vectors, one workgroup per
-// i8_cols_tile_rows rows with one wave per 16-vector column tile and row group
-// (LDS: two record slots of 256 bytes per row); otherwise one workgroup per
+// i8_cols_tile_rows rows with one wave per 16-vector column tile (LDS: two
+// record slots of 256 bytes per row); otherwise one workgroup per
 // 16-row matrix-core tile whose mfma_ksplit(k, rows) waves split k (the LDS
 // holds their partial accumulators and the weight staging tiles).
 int geo_i8(const int64_t *w, loom_launch_config *c) {
@@ -90,11 +90,9 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
         return set(c, tiles < kI8RowsGroups ? tiles : kI8RowsGroups, kSubgroupSize * kI8RowsWaves,
                    i8_rows_lds_bytes(chunks));
     }
-    if (w[2] > 16) {
-        const int nt = mfma_col_tiles(w[2]);
-        return set(c, ceil_div(w[0], i8_cols_tile_rows(nt, w[0])), kSubgroupSize * nt * i8_cols_row_groups(nt),
-                   i8_cols_lds_bytes(nt, w[0]));
-    }
+    if (w[2] > 16)
+        return set(c, ceil_div(w[0], i8_cols_tile_rows(w[0])), kSubgroupSize * mfma_col_tiles(w[2]),
+                   i8_cols_lds_bytes(w[0]));
     const int ks = mfma_ksplit(w[1], w[0]);
     return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * ks,
                (ks - 1) * 4 * kSubgroupSize * 4 + (kMfmaStage ? ks * kMfmaStageBytes : 0));

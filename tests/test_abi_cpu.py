@@ -120,7 +120,7 @@ def test_launch_config_tiles(loom):
     # each) + 4 per-wave 16x256 B weight staging tiles
     assert cfg["workgroup_size"] == (256, 1, 1)
     assert cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096
-    # more than 16 vectors, four column tiles (33-64): one wave per 16-vector
+    # more than 16 vectors, four column tiles: one wave per 16-vector
     # column tile, the 16-row tiles shared evenly by one or two workgroups per
     # CU (at most 8 tiles per wave); LDS: two record slots of 256 B per row
     for rows, rt, groups in ((16384, 4, 256), (28672, 7, 256), (24575, 6, 256), (24576, 6, 256), (4096, 1, 256),
@@ -129,10 +129,12 @@ def test_launch_config_tiles(loom):
         cfg = loom.launch_config_invoke(i8, [rows, 8192, 64])
         assert cfg["workgroups"][0] == groups == -(-rows // (16 * rt)), rows
         assert cfg["workgroup_size"] == (256, 1, 1) and cfg["workgroup_storage_bytes"] == 2 * 16 * rt * 256, rows
-    # two column tiles (17-32): 64 rows per workgroup, 2 waves
-    assert loom.launch_config_invoke(i8, [28672, 8192, 32])["workgroups"][0] == 448  # two column tiles: 64 rows
+    # 17-32 vectors take the same kernel and geometry (the unused column
+    # tiles are zeroed)
+    for batch in (17, 32, 33, 64):
+        assert loom.launch_config_invoke(i8, [28672, 8192, batch]) == loom.launch_config_invoke(i8, [28672, 8192, 64])
     cfg = loom.launch_config_invoke(i8, [100, 1000, 17])
-    assert cfg["workgroups"][0] == 2 and cfg["workgroup_size"] == (128, 1, 1)
+    assert cfg["workgroups"][0] == 7 and cfg["workgroup_size"] == (256, 1, 1)
     assert loom.launch_config_invoke(i8, [5, 64, 33])["workgroups"][0] == 1
     assert loom.launch_config_invoke(i8, [17, 64, 2])["workgroups"][0] == 2
     # 9-16 vectors, k a multiple of 1024 from 4096 to 8192: one 16-wave
@@ -362,7 +364,7 @@ def _kernel_metadata(lib_path, tmp_path):
 
 
 def test_column_kernel_shares_rows_evenly(loom):
-    # 33-64 vectors: for any row count, the 16-row tiles are split into
+    # more than 16 vectors: for any row count, the 16-row tiles are split into
     # workgroups of RT tiles (1 <= RT <= 8, read back from the LDS size),
     # q = ceil(tiles / 2048) workgroups per CU at most, and the last workgroup
     # still has rows
@@ -380,7 +382,7 @@ def test_column_kernel_shares_rows_evenly(loom):
 
 
 def test_column_kernel_fits_two_workgroups_per_cu(loom, tmp_path):
-    # 33-64 vectors over many rows run two 4-wave workgroups per CU, which
+    # more than 16 vectors over many rows run two 4-wave workgroups per CU, which
     # needs at most 256 registers per wave (two waves per SIMD); above that
     # the second workgroup of each CU waits for the first
     kernels = [(n, v) for n, _, v in _kernel_metadata(loom.LIB_PATH, tmp_path) if "i8_mfma_cols_kernel" in n]
