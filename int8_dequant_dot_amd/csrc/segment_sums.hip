@@ -69,18 +69,22 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
 }
 
 // Rows in flight per wave.  A launch of many waves (segments x 256-column
-// blocks) keeps HBM busy with 8 rows each (7 KiB per wave at 256 columns);
-// with few waves each needs a deeper ring.  Over ~1-4 GB: 16384 segments
-// (depth 8 / 16) 677.7 / 693.6 us; 2048 waves 734.9 / 735.3 / 721.0 us at
-// depth 8 / 16 / 32; 1024 waves (128 columns) 290.7 / 221.7; 512 waves 276.3
-// / 195.0 / 198.6; 128 waves 912.4 / 525.4 / 336.6 us.  The order of every
-// column's sum is the same at any depth.
+// blocks) over 256 columns keeps HBM busy with 8 rows each (7 KiB per wave);
+// few waves, or narrow rows (fewer bytes per row), need a deeper ring.  Over
+// ~1-4 GB at depth 8 / 16 / 32: 16384 segments of 256 columns 676.5 / 693.1 /
+// 684.4 us; 2048 waves 734.9 / 735.3 / 721.0; 512 waves 276.3 / 195.0 /
+// 198.6; 128 waves 912.4 / 525.4 / 336.6; 128 columns (8192 segments) 427.5
+// / 353.6 / 344.7; 64 columns (16384 segments) 677.5 / 458.4 / 444.8; 16
+// columns 1142.9 / 737.4 / 691.6 us.  The order of every column's sum is the
+// same at any depth.
 #ifndef LOOM_SEGMENT_SUMS_DEPTH
 #define LOOM_SEGMENT_SUMS_DEPTH 8
 #endif
 constexpr int kSegmentDepth = LOOM_SEGMENT_SUMS_DEPTH;
-constexpr int segment_sums_depth(int64_t waves) {
-    return waves <= 256 ? 4 * kSegmentDepth : waves <= 1024 ? 2 * kSegmentDepth : kSegmentDepth;
+constexpr int segment_sums_depth(int64_t waves, int cols) {
+    const int by_waves = waves <= 256 ? 4 * kSegmentDepth : waves <= 1024 ? 2 * kSegmentDepth : kSegmentDepth;
+    const int by_width = cols <= 64 ? 4 * kSegmentDepth : cols <= 128 ? 2 * kSegmentDepth : kSegmentDepth;
+    return by_waves > by_width ? by_waves : by_width;
 }
 
 template <int DEPTH>
@@ -110,7 +114,7 @@ hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, in
     const dim3 grid(cfg.workgroups[0], cfg.workgroups[1]), block(cfg.workgroup_size[0]);
     const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0) &&
                       (cols % 4 == 0);
-    switch (segment_sums_depth((int64_t)cfg.workgroups[0] * cfg.workgroups[1])) {
+    switch (segment_sums_depth((int64_t)cfg.workgroups[0] * cfg.workgroups[1], cols)) {
         case 4 * kSegmentDepth:
             launch_segment_sums_depth<4 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, cols, out,
                                                          tail_counts, stream);

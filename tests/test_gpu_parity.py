@@ -199,11 +199,13 @@ def test_segment_sums_exact(loom, device, lengths, cols):
 
 
 @pytest.mark.parametrize("segments,max_len,cols", [(200, 3000, 256), (600, 200, 256), (250, 300, 1000),
-                                                     (1100, 50, 256), (300, 64, 1000)])
+                                                     (1100, 50, 256), (300, 64, 1000), (1500, 100, 16),
+                                                     (1500, 100, 100), (1500, 100, 130)])
 def test_segment_sums_ring_depths(loom, device, segments, max_len, cols):
     # the read-ahead depth follows the wave count (segments x 256-column
-    # blocks): 32 rows up to 256 waves, 16 up to 1024, 8 above; every depth
-    # gives the same bits
+    # blocks: 32 rows up to 256 waves, 16 up to 1024, else 8) and the row
+    # width (32 up to 64 columns, 16 up to 128); every depth gives the same
+    # bits
     L = synth.segment_lengths(77, segments, max_len)
     off = synth.segment_offsets(L)
     x = synth.segment_rows(synth.SEGMENTS.seed, 0, int(off[-1]), cols)
