@@ -14,8 +14,10 @@
  *  - Return LOOM_OK (0) or a negative loom_status.  All argument checks run on
  *    the host before anything is enqueued; on error nothing is launched and no
  *    output is touched.  Sizes and counts are checked first (LOOM_ERR_RANGE,
- *    LOOM_ERR_SHAPE); a call with nothing to do (no rows, elements, segments,
- *    outputs or tokens) then returns LOOM_OK without looking at its pointers;
+ *    LOOM_ERR_SHAPE), including the launch grid's limit of fewer than 2^32
+ *    work-items (see each call); a call with nothing to do (no rows,
+ *    elements, segments, outputs or tokens) then returns LOOM_OK without
+ *    looking at its pointers;
  *    otherwise required pointers (LOOM_ERR_NULL) and then alignment
  *    (LOOM_ERR_ALIGN) are checked.
  *  - Data pointers are device pointers (HIP allocations of the current device,
@@ -24,7 +26,9 @@
  *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *    asynchronously on it; outputs are ready once the stream has reached the
  *    enqueued work.  A device-side fault is reported by later HIP calls, not
- *    by the return code; LOOM_ERR_DEVICE means the launch itself was refused.
+ *    by the return code; LOOM_ERR_DEVICE means the launch itself was refused
+ *    (the thread's last HIP error is cleared before each launch, so an error
+ *    left by an earlier, unrelated HIP call is never reported as this one).
  *  - Calls are thread-safe: the only shared state is an immutable table.
  *  - Matrices are row-major.  Packed int8: an int32 word j of a row holds the
  *    elements 4j..4j+3, element 4j+b in byte b (little-endian), two's
@@ -103,7 +107,8 @@ int loom_launch_config_invoke(uint32_t token, const uint64_t *workload_bits,
  * 256 work-items; work-items at or beyond n touch nothing, so out[n..] is   *
  * left as it was (1009 elements run on 4 workgroups).                       *
  *   in, out : f32[n], device, 4-byte aligned; may be NULL only when n == 0  *
- *   n       : 0 <= n <= 255 * (2^31 - 1) (LOOM_ERR_RANGE otherwise)         *
+ *   n       : 0 <= n <= 2^32 - 256, so the grid stays below 2^32           *
+ *             work-items (LOOM_ERR_RANGE otherwise)                         *
  * ------------------------------------------------------------------------ */
 int loom_copy_f32(const float *in, float *out, int64_t n, void *stream);
 
@@ -134,14 +139,17 @@ int loom_row_sum_tiles(const float *values, int64_t rows_alloc, int64_t count,
  * Every row is streamed with coalesced loads read ahead of the              *
  * accumulation and finished by cross-lane reductions; how rows map to the   *
  * GPU depends on their width: 1-128 floats are packed several to a 64-lane  *
- * record; 129-1023 floats run in full 8-row tiles plus one guarded tail     *
- * tile; a row of 1024 floats or more gets a workgroup of its own whose      *
- * wave totals are added in wave order.  f32 accumulation; the summation     *
+ * record; 129-768 floats run in full 8-row tiles plus one guarded tail      *
+ * tile; a row of 769 floats or more gets a workgroup of its own whose wave  *
+ * totals are added in wave order.  f32 accumulation; the summation          *
  * order inside a row is a fixed tree, the same on every call (error         *
  * <= 1e-5 * sum|x| for the documented sizes).                               *
  *   x          : f32, device, 4-byte aligned (16-byte alignment of x and    *
  *                row_stride % 4 == 0 select 128-bit loads)                  *
- *   rows, cols : 0 <= rows < 2^31, 0 <= cols < 2^31                         *
+ *   rows, cols : 0 <= rows < 2^31, 0 <= cols < 2^31; LOOM_ERR_RANGE also    *
+ *                when the grid would reach 2^32 work-items, as              *
+ *                loom_launch_config_invoke reports for (rows, cols): only   *
+ *                past 2^30 - 16 rows of at most 768 floats                  *
  *   row_stride : elements between row starts, row_stride >= cols            *
  *                (LOOM_ERR_SHAPE); 4 * rows * row_stride must fit in an     *
  *                int64 (LOOM_ERR_RANGE)                                     *
@@ -179,14 +187,17 @@ int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets
  *     acc[r][b] = sum_{i < k} w[r][i] * x[b][i]          (exact, int32)     *
  *     out[r][b] = (f32(acc[r][b]) * w_scale[r]) * x_scale[b]                *
  * with each product rounded once to f32; when x_scale is NULL the second    *
- * product is skipped.  One vector with k a multiple of 1024 or k >= 12288  *
- * runs a v_dot4 (int8x4) GEMV; every other call an int8 MFMA kernel.  The   *
- * results are the same bits either way.                                     *
+ * product is skipped.  One vector runs a v_dot4 (int8x4) GEMV: rows of up  *
+ * to 512 bytes packed several to a 1 KiB record, rows up to 4 KiB a wave    *
+ * per block of rows, longer rows a workgroup per row.  Several vectors run  *
+ * an int8 MFMA kernel.  The results are the same bits either way.           *
  *   w       : int32[rows][k/4] packed int8 weights, device, 4-byte aligned  *
  *   w_scale : f32[rows], device                                             *
  *   x       : int32[batch][k/4] packed int8 activations, device             *
  *   x_scale : f32[batch], device, or NULL (= 1)                             *
- *   rows    : 0 <= rows < 2^31                                              *
+ *   rows    : 0 <= rows < 2^31; LOOM_ERR_RANGE also when the grid would     *
+ *             reach 2^32 work-items, as loom_launch_config_invoke reports   *
+ *             for (rows, k, batch): only at 2^26 rows or more               *
  *   k       : elements per row, k % 4 == 0 (LOOM_ERR_SHAPE), 0 <= k <=      *
  *             131068 so |acc| <= 2^31 - 1 (LOOM_ERR_RANGE)                  *
  *   batch   : 1 <= batch <= 64 (LOOM_ERR_RANGE)                             *
@@ -215,7 +226,11 @@ int loom_i8_dequant_dot(const int32_t *w, const float *w_scale, const int32_t *x
  *   initial : f32[outputs] or NULL                                          *
  *   records : records allocated; 0 <= count <= records, count < 2^31, and   *
  *             4 * records * outputs fits in an int64 (LOOM_ERR_RANGE)     *
- *   outputs : 0 <= outputs <= 255 * (2^31 - 1)                              *
+ *   outputs : 0 <= outputs <= 255 * (2^31 - 1); LOOM_ERR_RANGE also when    *
+ *             the grid would reach 2^32 work-items, as                      *
+ *             loom_launch_config_invoke reports for (outputs, count,        *
+ *             streams): past 2^32 - 256 outputs, or 2^34 - 1024 when        *
+ *             streams divides 64                                            *
  *   out     : f32[outputs]                                                  *
  * ------------------------------------------------------------------------ */
 int loom_packed_dot(const int32_t *fields, const uint16_t *scales, const float *rhs, int64_t streams,

@@ -63,6 +63,18 @@ __device__ __forceinline__ T half_wave_sum(T v) {
     return v;
 }
 
+// Sum over each aligned group of 2^LOG2L lanes (LOG2L <= 5): the first
+// LOG2L steps of half_wave_sum.  Every lane of a group receives its sum.
+template <int LOG2L, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+    if constexpr (LOG2L >= 1) v = v + dpp<kDppQuadSwap1>(v);
+    if constexpr (LOG2L >= 2) v = v + dpp<kDppQuadSwap2>(v);
+    if constexpr (LOG2L >= 3) v = v + dpp<kDppHalfMirror>(v);
+    if constexpr (LOG2L >= 4) v = v + dpp<kDppMirror>(v);
+    if constexpr (LOG2L >= 5) v = v + swz16(v);
+    return v;
+}
+
 __device__ __forceinline__ float readlane(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }

@@ -25,6 +25,14 @@ enum ExportId : uint32_t {
 // `workload` holds the export's workload arguments; returns a loom_status.
 int evaluate_launch(ExportId id, const int64_t *workload, loom_launch_config *out);
 
+// HIP launches a grid only while grid.x * block.x stays below 2^32 work-items.
+constexpr int64_t kMaxGridWorkItems = (int64_t(1) << 32) - 1;
+// Workgroups of a grid-stride launch over `units` (workgroup b takes units
+// b, b + grid.x, ...): one per unit up to the work-item limit.
+constexpr int64_t grid_stride_groups(int64_t units, int64_t workgroup_size) {
+    return units < kMaxGridWorkItems / workgroup_size ? units : kMaxGridWorkItems / workgroup_size;
+}
+
 // Rows per full tile ("Tune loop unrolling and pipelining", §Derive full
 // tiles from a ragged loop).
 constexpr int kTileRows = 8;
@@ -75,35 +83,46 @@ constexpr int row_sums_waves_per_row(int64_t cols) {
 // ceil(cols / kSegmentBlockCols) waves (a 1 KiB record per row each).
 constexpr int kSegmentBlockCols = 256;
 
-// Blocking of the int8 kernels.  The v_dot4 GEMV gives each wave
-// gemv_rows_per_wave(k) consecutive rows, about 8 KiB of weights (one row at
-// k = 8192, at most 64 rows, one per lane of the result); the MFMA kernel
-// takes one 16-row matrix-core tile per workgroup, whose KSPLIT waves split
-// the k range and combine their int32 partials through LDS in wave order
-// (exact).  Tuning builds may override the macros.
+// Blocking of the int8 kernels.  One vector always runs a v_dot4 GEMV, in
+// one of three forms by row length k (bytes):
+//   narrow  k <= LOOM_GEMV_NARROW_MAX_K: several rows packed into each 1 KiB
+//           record, a wave per 64 rows;
+//   rows    up to LOOM_GEMV_WIDE_MIN_K: a wave per gemv_rows_per_wave(k)
+//           consecutive rows (about 8 KiB), each row one or more 1 KiB records;
+//   wide    longer rows: a workgroup of kGemvWideWaves waves per row.
+// Several vectors run an int8 MFMA kernel: one 16-row matrix-core tile per
+// workgroup, whose KSPLIT waves split the k range and combine their int32
+// partials through LDS in wave order (exact).  Tuning builds may override the
+// macros.
 #ifndef LOOM_GEMV_WAVE_BYTES
-#define LOOM_GEMV_WAVE_BYTES 8192  // 1 row per wave at k = 8192: 6% faster than 4-row tiles
+#define LOOM_GEMV_WAVE_BYTES 8192  // rows form: about 8 KiB of weights per wave
 #endif
-// One vector runs the GEMV when its rows are whole 1 KiB records (k a
-// multiple of 1024) or long (k >= LOOM_GEMV_ANY_K); other rows go to the
-// matrix-core tile kernel.  The GEMV reduces across the whole wave once per
-// row, and a row's last record is partly empty when k is not a multiple of
-// 1024.  Over 128 MiB of weights, the tile kernel took k = 512 from 76.3 to
-// 24.8 us, 1280 from 40.9 to 23.6, 2560 from 28.1 to 24.4; the GEMV kept
-// k = 1024 (20.9 against 23.5), 8192 (21.1 against 22.6) and 12800 (23.1
-// against 25.0).
-#ifndef LOOM_GEMV_MIN_K
-#define LOOM_GEMV_MIN_K 1024
+#ifndef LOOM_GEMV_NARROW_MAX_K
+#define LOOM_GEMV_NARROW_MAX_K 512
 #endif
-#ifndef LOOM_GEMV_ANY_K
-#define LOOM_GEMV_ANY_K 12288
+#ifndef LOOM_GEMV_WIDE_MIN_K
+#define LOOM_GEMV_WIDE_MIN_K 4096
 #endif
-constexpr bool i8_use_gemv(int64_t k, int64_t batch) {
-    return batch == 1 && k >= LOOM_GEMV_MIN_K && (k % 1024 == 0 || k >= LOOM_GEMV_ANY_K);
+constexpr int kGemvWideWaves = 4;
+enum GemvForm : int { kGemvNarrow = 0, kGemvRows = 1, kGemvWide = 2 };
+constexpr GemvForm gemv_form(int64_t k) {
+#ifdef LOOM_GEMV_FORCE_FORM
+    if (LOOM_GEMV_FORCE_FORM >= 0 && (LOOM_GEMV_FORCE_FORM != kGemvNarrow || k <= 512))
+        return (GemvForm)LOOM_GEMV_FORCE_FORM;
+#endif
+    return k <= LOOM_GEMV_NARROW_MAX_K ? kGemvNarrow : k < LOOM_GEMV_WIDE_MIN_K ? kGemvRows : kGemvWide;
 }
+constexpr bool i8_use_gemv(int64_t k, int64_t batch) { return batch == 1 && k >= 0; }
 constexpr int gemv_rows_per_wave(int64_t k_words) {
     const int64_t r = k_words > 0 ? LOOM_GEMV_WAVE_BYTES / (4 * k_words) : 64;
     return r < 1 ? 1 : r > 64 ? 64 : (int)r;
+}
+// narrow form: log2 of the lanes per row, the smallest L with 4 L >= k_words
+// (at most 32 lanes, so at least two rows per record)
+constexpr int gemv_narrow_log2_lanes(int64_t k_words) {
+    int l = 0;
+    while ((int64_t(4) << l) < k_words) ++l;
+    return l;
 }
 // Waves per 16-row tile of the tile kernel, each taking a contiguous 1/KS of
 // k: about 2 KiB of every row per wave.  Over ~224 MiB of weights with 2 and
@@ -213,8 +232,8 @@ hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *valu
 hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int rows, int cols,
                            int64_t row_stride, float *out, hipStream_t stream);
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
-                               const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
-                               hipStream_t stream);
+                               const int64_t *offsets, int64_t segments, int cols, float *out,
+                               int32_t *tail_counts, hipStream_t stream);
 hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,
                                  const int32_t *x, const float *x_scale, int rows, int k_words,
                                  int batch, float *out, int32_t *acc, hipStream_t stream);
@@ -227,7 +246,7 @@ hipError_t launch_sum_guarded_rows(const loom_launch_config &cfg, const float *v
                                    int active_lanes, float *sums, hipStream_t stream);
 
 hipError_t launch_routed_combine(const loom_launch_config &cfg, const int32_t *ids, const float *weights,
-                                 const float *payload, int64_t num_rows, int routes, int hidden, float *out,
-                                 hipStream_t stream);
+                                 const float *payload, int64_t num_rows, int64_t tokens, int routes, int hidden,
+                                 float *out, hipStream_t stream);
 
 }  // namespace loom

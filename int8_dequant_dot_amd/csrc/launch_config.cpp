@@ -15,10 +15,10 @@ namespace loom {
 namespace {
 
 constexpr uint32_t kSubgroupSize = 64;             // gfx950 wave64
-constexpr int64_t kMaxGridX = 0x7FFFFFFF;          // HIP grid.x limit, in workgroups
 
 int set(loom_launch_config *c, int64_t workgroups, uint32_t workgroup_size, uint32_t storage) {
-    if (workgroups < 0 || workgroups > kMaxGridX) return LOOM_ERR_RANGE;
+    // HIP launches a grid only while grid.x * block.x < 2^32 work-items
+    if (workgroups < 0 || workgroups * (int64_t)workgroup_size > kMaxGridWorkItems) return LOOM_ERR_RANGE;
     c->workgroups[0] = (uint32_t)workgroups;
     c->workgroups[1] = 1;
     c->workgroups[2] = 1;
@@ -54,28 +54,32 @@ int geo_row_sum_tiles(const int64_t *w, loom_launch_config *c) {
 
 // row_sums(rows, cols): narrow rows (1-128 columns) several to a record, one
 // wave per kRowSumsNarrowRecords records; long rows (row_sums_waves_per_row > 0) one workgroup
-// per row; the others one wave per block of kRowSumsTilesPerWave tiles of 8
+// per row (each taking every grid.x-th row once the grid reaches 2^32
+// work-items); the others one wave per block of kRowSumsTilesPerWave tiles of 8
 // rows (the last tile the tail).
 int geo_row_sums(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
     if (row_sums_narrow_log2_lanes(w[1]) >= 0)
         return set(c, ceil_div(w[0], row_sums_narrow_rows_per_wave(w[1])), kSubgroupSize, 0);
-    if (const int waves = row_sums_waves_per_row(w[1]))
-        return set(c, w[0], kSubgroupSize * waves, 4 * kRowSumsWideMaxWaves);  // LDS: the wave totals
+    if (const int waves = row_sums_waves_per_row(w[1]))  // LDS: the wave totals
+        return set(c, grid_stride_groups(w[0], kSubgroupSize * waves), kSubgroupSize * waves,
+                   4 * kRowSumsWideMaxWaves);
     return set(c, ceil_div(w[0], int64_t(kTileRows) * kRowSumsTilesPerWave), kSubgroupSize, 0);
 }
 
 // segment_sums(segments, cols): one wave per segment and block of
 // kSegmentBlockCols columns (at least one block, which also writes the
-// segment's tail count when there are no columns).
+// segment's tail count when there are no columns); past 2^26 - 1 segments
+// each wave takes every grid.x-th segment.
 int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
     const int64_t blocks = w[1] > 0 ? ceil_div(w[1], kSegmentBlockCols) : 1;
-    return set2(c, w[0], blocks, kSubgroupSize, 0);
+    return set2(c, grid_stride_groups(w[0], kSubgroupSize), blocks, kSubgroupSize, 0);
 }
 
-// i8_dequant_dot(rows, k, batch): for one vector and k that i8_use_gemv
-// admits, one wave per block of gemv_rows_per_wave(k) rows; for 9 to 16 vectors and k a multiple of 1024
+// i8_dequant_dot(rows, k, batch): for one vector, by gemv_form(k), one wave
+// per 64 short rows, one wave per block of gemv_rows_per_wave(k) rows, or one
+// workgroup of kGemvWideWaves waves per long row; for 9 to 16 vectors and k a multiple of 1024
 // from 4096 to 8192, one 16-wave workgroup per CU (at most one per 16-row
 // tile) that walks the tiles; for more than 16 vectors, one workgroup per
 // i8_cols_tile_rows rows with one wave per 16-vector column tile (LDS: two
@@ -84,7 +88,15 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 // holds their partial accumulators and the weight staging tiles).
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
-    if (i8_use_gemv(w[1], w[2])) return set(c, ceil_div(w[0], gemv_rows_per_wave(w[1] / 4)), kSubgroupSize, 0);
+    if (i8_use_gemv(w[1], w[2])) {
+        switch (gemv_form(w[1])) {
+            case kGemvNarrow: return set(c, ceil_div(w[0], kSubgroupSize), kSubgroupSize, 0);
+            case kGemvRows: return set(c, ceil_div(w[0], gemv_rows_per_wave(w[1] / 4)), kSubgroupSize, 0);
+            default:  // LDS: the wave totals
+                return set(c, grid_stride_groups(w[0], kSubgroupSize * kGemvWideWaves),
+                           kSubgroupSize * kGemvWideWaves, 4 * kGemvWideWaves);
+        }
+    }
     if (const int chunks = i8_rows_chunks(w[0], w[1], w[2])) {
         const int64_t tiles = ceil_div(w[0], kMfmaTileRows);
         return set(c, tiles < kI8RowsGroups ? tiles : kI8RowsGroups, kSubgroupSize * kI8RowsWaves,
@@ -112,10 +124,12 @@ int geo_sum_guarded_rows(const int64_t *w, loom_launch_config *c) {
     return set(c, 1, 32, 0);
 }
 
-// routed_combine(tokens, routes, hidden): one wave per token and column block.
+// routed_combine(tokens, routes, hidden): one wave per token and column block
+// (past 2^26 - 1 tokens, each wave takes every grid.x-th token).
 int geo_routed_combine(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 0) return LOOM_ERR_RANGE;
-    return set2(c, w[0], ceil_div(w[2], kRoutedColumnsPerWave), kSubgroupSize, 0);
+    return set2(c, grid_stride_groups(w[0], kSubgroupSize), ceil_div(w[2], kRoutedColumnsPerWave), kSubgroupSize,
+                0);
 }
 
 struct Export {

@@ -4,8 +4,8 @@
 // row sums pick one of three mappings by row width (row_sums_narrow_log2_lanes
 // and row_sums_waves_per_row choose; the launch table uses the same rules):
 //   1-128 floats      several rows packed into each 64-lane record
-//   129-1023 floats   one wave per 2 full 8-row tiles, the last tile the tail
-//   1024+ floats      one workgroup per row, its columns split over 1-16 waves
+//   129-768 floats    one wave per 2 full 8-row tiles, the last tile the tail
+//   769+ floats       one workgroup per row, its columns split over 1-16 waves
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kWave) void row_sum_tiles_kernel(const float *__res
 }
 
 // ----------------------------------------------------------------------------
-// Streaming row sums of rows of 129-1023 floats.  One wave owns
+// Streaming row sums of rows of 129-768 floats.  One wave owns
 // kRowSumsTilesPerWave consecutive tiles of 8 rows (the last tile of the
 // matrix holds the rows mod 8 tail, so it is the separate guarded tile of
 // TUNE §Derive full tiles).  The wave's rows are walked as one stream of
@@ -128,7 +128,8 @@ __global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict
 }
 
 // ----------------------------------------------------------------------------
-// Row sums of long rows (1024 columns and more).  One workgroup of
+// Row sums of long rows (769 columns and more: at least four 256-float
+// records, the last one possibly partial).  One workgroup of
 // W = blockDim.x / 64 waves owns one row; wave w streams a contiguous share of
 // the row's records (the same 64 x VEC float records as above, about four per
 // wave) into a private partial, reduces it across the wave, and the W wave
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(kWave) void row_sums_kernel(const float *__restrict
 // ----------------------------------------------------------------------------
 template <int VEC, bool FULL, int DEPTH>
 __global__ __launch_bounds__(kWave * kRowSumsWideMaxWaves) void row_sums_wide_kernel(const float *__restrict__ x,
-                                                                                   int cols, int64_t row_stride,
+                                                                                   int rows, int cols,
+                                                                                   int64_t row_stride,
                                                                                    float *__restrict__ out) {
     typedef typename vec_of<VEC>::type V;
     constexpr int kBlock = kWave * VEC;
@@ -148,32 +150,36 @@ __global__ __launch_bounds__(kWave * kRowSumsWideMaxWaves) void row_sums_wide_ke
     const int waves = blockDim.x / kWave;
     // the same in every lane: keeps the wave's share and cursor in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    const int64_t row = blockIdx.x;
-    const int records = (cols + kBlock - 1) / kBlock;
+    // (no cols + kBlock - 1: that overflows for rows close to 2^31 floats)
+    const int records = cols / kBlock + (cols % kBlock != 0);
     const int per = (records + waves - 1) / waves;
     const int first = min(records, wave * per);
     const int n = min(records, first + per) - first;
-    const float *rp = x + row * row_stride;
-    int64_t lcol = (int64_t)first * kBlock;
     const int lane_col = lane * VEC;
-    V acc = V(0.0f);
-    pipelined<DEPTH, V>(
-        n,
-        [&]() {
-            V v = V(0.0f);
-            if (FULL || lane_col < cols - lcol) v = load_stream(reinterpret_cast<const V *>(rp + lcol + lane_col));
-            lcol += kBlock;
-            return v;
-        },
-        [&](V v) { acc += v; });
-    const float total = wave_sum(fold<VEC>(acc));
     __shared__ float part[kRowSumsWideMaxWaves];
-    if (lane == 0) part[wave] = total;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float sum = 0.0f;
-        for (int w = 0; w < waves; ++w) sum = sum + part[w];
-        out[row] = sum;
+    // one row per workgroup; past the grid's work-item limit, every grid.x-th row
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const float *rp = x + row * row_stride;
+        int64_t lcol = (int64_t)first * kBlock;
+        V acc = V(0.0f);
+        pipelined<DEPTH, V>(
+            n,
+            [&]() {
+                V v = V(0.0f);
+                if (FULL || lane_col < cols - lcol) v = load_stream(reinterpret_cast<const V *>(rp + lcol + lane_col));
+                lcol += kBlock;
+                return v;
+            },
+            [&](V v) { acc += v; });
+        const float total = wave_sum(fold<VEC>(acc));
+        if (lane == 0) part[wave] = total;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float sum = 0.0f;
+            for (int w = 0; w < waves; ++w) sum = sum + part[w];
+            out[row] = sum;
+        }
+        if (row + gridDim.x < rows) __syncthreads();  // part[] is rewritten for the next row
     }
 }
 
@@ -190,16 +196,6 @@ __global__ __launch_bounds__(kWave * kRowSumsWideMaxWaves) void row_sums_wide_ke
 // instructions on every path, the producer never waits on its own loads,
 // and the read-ahead keeps its partial waits.
 // ----------------------------------------------------------------------------
-template <int LOG2L>
-__device__ __forceinline__ float group_sum(float v) {
-    if constexpr (LOG2L >= 1) v = v + dpp<kDppQuadSwap1>(v);
-    if constexpr (LOG2L >= 2) v = v + dpp<kDppQuadSwap2>(v);
-    if constexpr (LOG2L >= 3) v = v + dpp<kDppHalfMirror>(v);
-    if constexpr (LOG2L >= 4) v = v + dpp<kDppMirror>(v);
-    if constexpr (LOG2L >= 5) v = v + swz16(v);
-    return v;
-}
-
 template <bool VEC4, int LOG2L, int DEPTH>
 __global__ __launch_bounds__(kWave) void row_sums_narrow_kernel(const float *__restrict__ x, int rows, int cols,
                                                                 int64_t row_stride, float *__restrict__ out) {
@@ -293,13 +289,13 @@ hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int ro
     }
     if (row_sums_waves_per_row(cols) > 0) {
         if (vec4 && cols % (kWave * 4) == 0)
-            row_sums_wide_kernel<4, true, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);
+            row_sums_wide_kernel<4, true, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);
         else if (vec4)
-            row_sums_wide_kernel<4, false, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);
+            row_sums_wide_kernel<4, false, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);
         else if (cols % kWave == 0)
-            row_sums_wide_kernel<1, true, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);
+            row_sums_wide_kernel<1, true, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);
         else
-            row_sums_wide_kernel<1, false, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, cols, row_stride, out);
+            row_sums_wide_kernel<1, false, kRowSumsWideDepth><<<grid, block, 0, stream>>>(x, rows, cols, row_stride, out);
         return hipGetLastError();
     }
     if (vec4) {

@@ -28,43 +28,45 @@ template <> struct seg_vec<4> { typedef float4v type; };
 // ----------------------------------------------------------------------------
 template <int VEC, bool FULL, int DEPTH>
 __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__restrict__ x, int64_t total_rows,
-                                                             const int64_t *__restrict__ offsets, int cols,
-                                                             float *__restrict__ out,
+                                                             const int64_t *__restrict__ offsets, int64_t segments,
+                                                             int cols, float *__restrict__ out,
                                                              int32_t *__restrict__ tail_counts) {
     typedef typename seg_vec<VEC>::type V;
     constexpr int kBlock = kWave * VEC;
     const int lane = lane_id();
-    const int64_t s = blockIdx.x;
     const int block_first = blockIdx.y * kSegmentBlockCols;
     const int block_end = min(cols, block_first + kSegmentBlockCols);
-    const int64_t begin = offsets[s];
-    const int64_t end = offsets[s + 1];
-    float *o = out + s * cols;
+    // one segment per wave; past the grid's work-item limit, every grid.x-th segment
+    for (int64_t s = blockIdx.x; s < segments; s += gridDim.x) {
+        const int64_t begin = offsets[s];
+        const int64_t end = offsets[s + 1];
+        float *o = out + s * cols;
 
-    if (!(begin >= 0 && begin <= end && end <= total_rows)) {
-        for (int c = block_first + lane; c < block_end; c += kWave) o[c] = __builtin_nanf("");
-        if (lane == 0 && blockIdx.y == 0 && tail_counts) tail_counts[s] = -1;
-        return;
-    }
-    const int64_t length = end - begin;
-    if (lane == 0 && blockIdx.y == 0 && tail_counts) tail_counts[s] = (int32_t)(length & (kTileRows - 1));
+        if (!(begin >= 0 && begin <= end && end <= total_rows)) {
+            for (int c = block_first + lane; c < block_end; c += kWave) o[c] = __builtin_nanf("");
+            if (lane == 0 && blockIdx.y == 0 && tail_counts) tail_counts[s] = -1;
+            continue;
+        }
+        const int64_t length = end - begin;
+        if (lane == 0 && blockIdx.y == 0 && tail_counts) tail_counts[s] = (int32_t)(length & (kTileRows - 1));
 
-    for (int cb = block_first; cb < block_end; cb += kBlock) {
-        const int c = cb + lane * VEC;
-        const bool active = FULL || c < cols;
-        // Row base of the next load (wave-uniform) plus the lane's column.
-        const float *rp = x + begin * cols + cb;
-        const int lane_col = active ? lane * VEC : -cb;  // inactive lanes read the row's first columns
-        V acc = V(0.0f);
-        pipelined<DEPTH, V>(
-            length,
-            [&]() {
-                const V v = load_stream(reinterpret_cast<const V *>(rp + lane_col));
-                rp += cols;
-                return v;
-            },
-            [&](V v) { acc += v; });
-        if (active) *reinterpret_cast<V *>(o + c) = acc;
+        for (int cb = block_first; cb < block_end; cb += kBlock) {
+            const int c = cb + lane * VEC;
+            const bool active = FULL || c < cols;
+            // Row base of the next load (wave-uniform) plus the lane's column.
+            const float *rp = x + begin * cols + cb;
+            const int lane_col = active ? lane * VEC : -cb;  // inactive lanes read the row's first columns
+            V acc = V(0.0f);
+            pipelined<DEPTH, V>(
+                length,
+                [&]() {
+                    const V v = load_stream(reinterpret_cast<const V *>(rp + lane_col));
+                    rp += cols;
+                    return v;
+                },
+                [&](V v) { acc += v; });
+            if (active) *reinterpret_cast<V *>(o + c) = acc;
+        }
     }
 }
 
@@ -89,43 +91,43 @@ constexpr int segment_sums_depth(int64_t waves, int cols) {
 
 template <int DEPTH>
 static void launch_segment_sums_depth(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
-                                      const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
-                                      hipStream_t stream) {
+                                      const int64_t *offsets, int64_t segments, int cols, float *out,
+                                      int32_t *tail_counts, hipStream_t stream) {
     if (vec4) {
         if (cols % (kWave * 4) == 0)
-            segment_sums_kernel<4, true, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out,
+            segment_sums_kernel<4, true, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, segments, cols, out,
                                                                             tail_counts);
         else
-            segment_sums_kernel<4, false, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out,
+            segment_sums_kernel<4, false, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, segments, cols, out,
                                                                              tail_counts);
     } else {
         if (cols % kWave == 0)
-            segment_sums_kernel<1, true, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out,
+            segment_sums_kernel<1, true, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, segments, cols, out,
                                                                             tail_counts);
         else
-            segment_sums_kernel<1, false, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, cols, out,
+            segment_sums_kernel<1, false, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, segments, cols, out,
                                                                              tail_counts);
     }
 }
 
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
-                               const int64_t *offsets, int cols, float *out, int32_t *tail_counts,
-                               hipStream_t stream) {
+                               const int64_t *offsets, int64_t segments, int cols, float *out,
+                               int32_t *tail_counts, hipStream_t stream) {
     const dim3 grid(cfg.workgroups[0], cfg.workgroups[1]), block(cfg.workgroup_size[0]);
     const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0) &&
                       (cols % 4 == 0);
     switch (segment_sums_depth((int64_t)cfg.workgroups[0] * cfg.workgroups[1], cols)) {
         case 4 * kSegmentDepth:
-            launch_segment_sums_depth<4 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, cols, out,
-                                                         tail_counts, stream);
+            launch_segment_sums_depth<4 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, segments, cols,
+                                                         out, tail_counts, stream);
             break;
         case 2 * kSegmentDepth:
-            launch_segment_sums_depth<2 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, cols, out,
-                                                         tail_counts, stream);
+            launch_segment_sums_depth<2 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, segments, cols,
+                                                         out, tail_counts, stream);
             break;
         default:
-            launch_segment_sums_depth<kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, cols, out,
-                                                     tail_counts, stream);
+            launch_segment_sums_depth<kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, segments, cols,
+                                                     out, tail_counts, stream);
             break;
     }
     return hipGetLastError();

@@ -65,20 +65,38 @@ def _mis(p, a):
     return p is not None and p % a != 0
 
 
+def _grid_refused(export, workload):
+    """The header's rule for the grid limit: a workload whose launch grid would
+    reach 2^32 work-items is refused with LOOM_ERR_RANGE, as the launch table
+    reports it for the same workload (only evaluated when every documented
+    size range holds)."""
+    import int8_dequant_dot_amd as loom
+    try:
+        loom.launch_config_invoke(loom.launch_config_lookup(export), workload)
+    except loom.LoomError as e:
+        assert e.status == RANGE
+        return True
+    return False
+
+
 @SETTINGS
-@given(x=PTRS, out=PTRS, rows=sizes(I31), cols=sizes(I31), stride=sizes(I31))
+@given(x=PTRS, out=PTRS, rows=sizes(I31, 2**30 - 16, 2**31 - 32), cols=sizes(I31, 768, 64), stride=sizes(I31))
 def test_row_sums_contract(lib, x, out, rows, cols, stride):
-    expect = _status([(RANGE, not (0 <= rows <= I31 and 0 <= cols <= I31)), (SHAPE, stride < cols),
-                      (RANGE, rows > 0 and 4 * rows * stride > I64)],
+    in_range = 0 <= rows <= I31 and 0 <= cols <= I31
+    expect = _status([(RANGE, not in_range), (SHAPE, stride < cols),
+                      (RANGE, rows > 0 and 4 * rows * stride > I64),
+                      (RANGE, _grid_refused("row_sums", [rows, cols]))],
                      rows == 0, out is None or (x is None and cols > 0), _mis(x, 4) or _mis(out, 4))
     assert lib.loom_row_sums(_p(x), rows, cols, stride, _p(out), None) == expect
 
 
 @SETTINGS
-@given(w=PTRS, ws=PTRS, x=PTRS, xs=PTRS, out=PTRS, acc=PTRS, rows=sizes(I31), k=sizes(131068, 2**20),
+@given(w=PTRS, ws=PTRS, x=PTRS, xs=PTRS, out=PTRS, acc=PTRS, rows=sizes(I31, 2**26, 2**28), k=sizes(131068, 2**20),
        batch=sizes(64))
 def test_i8_dequant_dot_contract(lib, w, ws, x, xs, out, acc, rows, k, batch):
-    expect = _status([(RANGE, not (0 <= k <= 131068 and 1 <= batch <= 64 and 0 <= rows <= I31)), (SHAPE, k % 4 != 0)],
+    in_range = 0 <= k <= 131068 and 1 <= batch <= 64 and 0 <= rows <= I31
+    expect = _status([(RANGE, not in_range), (SHAPE, k % 4 != 0),
+                      (RANGE, _grid_refused("i8_dequant_dot", [rows, k, batch]))],
                      rows == 0, ws is None or out is None or (k > 0 and (w is None or x is None)),
                      any(_mis(p, 4) for p in (w, x, ws, xs, out, acc)))
     assert lib.loom_i8_dequant_dot(_p(w), _p(ws), _p(x), _p(xs), rows, k, batch, _p(out), _p(acc), None) == expect
@@ -96,11 +114,12 @@ def test_segment_sums_contract(lib, x, off, out, tails, total, segments, cols):
 
 @SETTINGS
 @given(f=PTRS, sc=PTRS, rhs=PTRS, init=PTRS, out=PTRS, streams=sizes(I31), records=sizes(I31, 2**40),
-       count=sizes(I31), outputs=sizes(255 * I31, 2**40))
+       count=sizes(I31), outputs=sizes(255 * I31, 2**40, 2**32 - 256, 2**34 - 1024))
 def test_packed_dot_contract(lib, f, sc, rhs, init, out, streams, records, count, outputs):
     expect = _status([(RANGE, not (0 <= count <= records and count <= I31 and 0 <= outputs <= 255 * I31
                                    and 1 <= streams <= I31)),
-                      (RANGE, records > 0 and 4 * records * outputs > I64)],
+                      (RANGE, records > 0 and 4 * records * outputs > I64),
+                      (RANGE, _grid_refused("packed_dot", [outputs, count, streams]))],
                      outputs == 0, out is None or (count > 0 and (f is None or sc is None or rhs is None)),
                      _mis(f, 4) or _mis(sc, 2) or _mis(rhs, 16) or _mis(init, 4) or _mis(out, 4))
     assert lib.loom_packed_dot(_p(f), _p(sc), _p(rhs), streams, _p(init), records, count, outputs, _p(out),
@@ -121,8 +140,8 @@ def test_routed_combine_contract(lib, ids, wts, pay, out, num_rows, tokens, rout
 
 
 @SETTINGS
-@given(inp=PTRS, out=PTRS, n=sizes(255 * I31))
+@given(inp=PTRS, out=PTRS, n=sizes(2**32 - 256, 255 * I31))
 def test_copy_contract(lib, inp, out, n):
-    expect = _status([(RANGE, not (0 <= n <= 255 * I31))], n == 0, inp is None or out is None,
+    expect = _status([(RANGE, not (0 <= n <= 2**32 - 256))], n == 0, inp is None or out is None,
                      _mis(inp, 4) or _mis(out, 4))
     assert lib.loom_copy_f32(_p(inp), _p(out), n, None) == expect

@@ -80,7 +80,7 @@ def test_launch_config_page_example(loom):
 
 def test_launch_config_matches_oracle_geometry(loom):
     tok = loom.launch_config_lookup("copy_f32")
-    for n in list(range(0, 2050)) + [2 ** 31, 2 ** 33 + 5]:
+    for n in list(range(0, 2050)) + [2 ** 31, 2 ** 32 - 256]:
         assert loom.launch_config_invoke(tok, [n])["workgroups"][0] == oracle.fill_workgroups(n, 256)
 
 
@@ -105,15 +105,21 @@ def test_launch_config_tiles(loom):
     assert loom.launch_config_invoke(seg, [100, 1000])["workgroups"] == (100, 4, 1)  # a wave per 256 columns
     assert loom.launch_config_invoke(seg, [5, 0])["workgroups"] == (5, 1, 1)  # still writes the tail counts
     i8 = loom.launch_config_lookup("i8_dequant_dot")
-    assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 16384  # one 8 KiB row per wave
-    # one vector: the GEMV for whole 1 KiB records or k >= 12288, else the
-    # matrix-core tile kernel (one wave per 16-row tile below k = 4096)
-    assert loom.launch_config_invoke(i8, [100, 1024, 1])["workgroups"] == (13, 1, 1)  # 8 rows per wave
-    assert loom.launch_config_invoke(i8, [100, 12804, 1])["workgroups"] == (100, 1, 1)
-    for k in (0, 4, 512, 1028, 1536, 2560, 8704):
+    # one vector, always a v_dot4 GEMV: rows of 4 KiB or more a 4-wave
+    # workgroup per row (LDS: the 4 wave totals) ...
+    for k in (4096, 4100, 8192, 8704, 12804, 131068):
         cfg = loom.launch_config_invoke(i8, [100, k, 1])
-        assert cfg["workgroups"] == (7, 1, 1) and cfg["workgroup_size"][0] == 64 * (2 if k >= 4096 else 1) * (
-            2 if k >= 8192 else 1), k
+        assert cfg["workgroups"] == (100, 1, 1) and cfg["workgroup_size"] == (256, 1, 1), k
+        assert cfg["workgroup_storage_bytes"] == 16, k
+    assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 16384
+    # ... rows of 513 bytes to 4 KiB a wave per block of about 8 KiB of rows ...
+    for k, rows_per_wave in ((516, 15), (1024, 8), (1028, 7), (1536, 5), (2560, 3), (4092, 2)):
+        cfg = loom.launch_config_invoke(i8, [100, k, 1])
+        assert cfg["workgroups"] == (-(-100 // rows_per_wave), 1, 1) and cfg["workgroup_size"] == (64, 1, 1), k
+    # ... and rows of up to 512 bytes a wave per 64 rows, several rows per record
+    for k in (0, 4, 16, 100, 256, 512):
+        cfg = loom.launch_config_invoke(i8, [100, k, 1])
+        assert cfg["workgroups"] == (2, 1, 1) and cfg["workgroup_size"] == (64, 1, 1), k
     cfg = loom.launch_config_invoke(i8, [28672, 8192, 8])
     assert cfg["workgroups"][0] == 1792
     # 4 waves split k per 16-row tile; LDS: 3 waves' int32 partial tiles (1 KiB
@@ -182,6 +188,36 @@ def test_launch_config_errors(loom, lib):
     with pytest.raises(loom.LoomError) as e:  # grid beyond 2^31-1 workgroups
         loom.launch_config_invoke(loom.launch_config_lookup("copy_f32"), [2 ** 31 * 256])
     assert e.value.status == loom.ERR_RANGE
+    # a grid of 2^32 work-items or more is never launched (HIP refuses it):
+    # one element per work-item stops at 2^32 - 256 elements ...
+    copy = loom.launch_config_lookup("copy_f32")
+    assert loom.launch_config_invoke(copy, [2 ** 32 - 256])["workgroups"][0] == 2 ** 24 - 1
+    for n in (2 ** 32 - 255, 2 ** 32, 2 ** 33 + 5):
+        with pytest.raises(loom.LoomError) as e:
+            loom.launch_config_invoke(copy, [n])
+        assert e.value.status == loom.ERR_RANGE
+    # ... while the kernels with a unit per workgroup take every grid.x-th unit
+    # past the limit (segments, long rows, tokens, long GEMV rows)
+    cap64, cap256 = (2 ** 32 - 1) // 64, (2 ** 32 - 1) // 256
+    seg = loom.launch_config_lookup("segment_sums")
+    assert loom.launch_config_invoke(seg, [cap64, 256])["workgroups"] == (cap64, 1, 1)
+    assert loom.launch_config_invoke(seg, [cap64 + 1, 256])["workgroups"] == (cap64, 1, 1)
+    assert loom.launch_config_invoke(seg, [2 ** 31 - 2, 1000])["workgroups"] == (cap64, 4, 1)
+    rs = loom.launch_config_lookup("row_sums")
+    assert loom.launch_config_invoke(rs, [2 ** 24, 4096])["workgroups"] == (cap256, 1, 1)
+    assert loom.launch_config_invoke(rs, [2 ** 31 - 1, 1 << 24])["workgroups"] == ((2 ** 32 - 1) // 1024, 1, 1)
+    assert loom.launch_config_invoke(rs, [2 ** 30 - 16, 768])["workgroups"] == (2 ** 26 - 1, 1, 1)
+    with pytest.raises(loom.LoomError) as e:  # row tiles: 4 work-items per row
+        loom.launch_config_invoke(rs, [2 ** 30 - 15, 768])
+    assert e.value.status == loom.ERR_RANGE
+    rt = loom.launch_config_lookup("routed_combine")
+    assert loom.launch_config_invoke(rt, [2 ** 26, 8, 1024])["workgroups"] == (cap64, 1, 1)
+    i8 = loom.launch_config_lookup("i8_dequant_dot")
+    assert loom.launch_config_invoke(i8, [2 ** 31 - 1, 8192, 1])["workgroups"] == (cap256, 1, 1)
+    with pytest.raises(loom.LoomError) as e:  # 16-row tiles of 4 waves: 16 work-items per row
+        loom.launch_config_invoke(i8, [2 ** 28, 8192, 8])
+    assert e.value.status == loom.ERR_RANGE
+    assert loom.launch_config_invoke(i8, [2 ** 28 - 16, 8192, 8])["workgroups"] == (2 ** 24 - 1, 1, 1)
     assert lib.loom_launch_config_lookup(None, None) == loom.ERR_NULL
     assert lib.loom_launch_config_invoke(tok, None, 2, None) == loom.ERR_NULL
     assert sorted(loom.EXPORTS) == sorted(
@@ -371,14 +407,23 @@ def test_column_kernel_shares_rows_evenly(loom):
     rng = np.random.default_rng(12)
     i8 = loom.launch_config_lookup("i8_dequant_dot")
     counts = list(rng.integers(1, 2**31 - 1, 300)) + [1, 16, 17, 4095, 4096, 4097, 32768, 32769, 2**31 - 1]
+    refused = 0
     for rows in map(int, counts):
-        cfg = loom.launch_config_invoke(i8, [rows, 64, 64])
+        try:
+            cfg = loom.launch_config_invoke(i8, [rows, 64, 64])
+        except loom.LoomError as e:
+            # 8 tiles per workgroup at most: 2^32 work-items or more only past 2^31 - 128 rows
+            assert e.status == loom.ERR_RANGE and rows > 2**31 - 128, rows
+            refused += 1
+            continue
         rt = cfg["workgroup_storage_bytes"] // (2 * 16 * 256)
         assert cfg["workgroup_storage_bytes"] == rt * 2 * 16 * 256 and 1 <= rt <= 8, rows
         tiles = -(-rows // 16)
         groups = cfg["workgroups"][0]
         assert groups == -(-rows // (16 * rt)) and (groups - 1) * 16 * rt < rows, rows
         assert groups <= 256 * -(-tiles // 2048), rows
+        assert groups * 256 < 2**32, rows
+    assert refused <= 1
 
 
 def test_column_kernel_fits_two_workgroups_per_cu(loom, tmp_path):

@@ -139,3 +139,71 @@ def test_packed_dot_fields_past_4gib(loom, device):
     del fields, scales
     ref = oracle.packed_dot(fs, ss, np.ascontiguousarray(rs), records, init)[0]
     assert np.array_equal(_bits(g[sample]), _bits(ref))
+
+
+@pytest.mark.parametrize("cols", [2**31 - 4, 2**31 - 1])
+def test_row_sums_one_row_of_nearly_2_31_floats(loom, device, cols):
+    # the longest row the header admits, on the 128-bit path (cols % 4 == 0)
+    # and on the 32-bit path: the record count of such a row must not
+    # overflow 32-bit arithmetic
+    x = torch.empty(1, cols, device=device)
+    synth.fill_chunked(x, synth.uniform_pm1, synth.DENSE.seed, synth.S_VALUES)
+    g = _np(loom.row_sums(x))
+    host = x.cpu().numpy()
+    del x
+    ref, d, a = oracle.row_sums(host)
+    bound = REL_SUM * a + 1e-30
+    assert abs(float(g[0]) - float(ref[0])) <= bound[0] and abs(float(g[0]) - float(d[0])) <= bound[0], cols
+
+
+def test_segment_sums_past_grid_limit(loom, device):
+    # 2^26 + 5 segments of 4 columns: more one-wave segments than a grid of
+    # fewer than 2^32 work-items holds, so some waves take two segments
+    S, cols = 2**26 + 5, 4
+    L = synth.randint(91, synth.S_LENGTHS, 0, S, 0, 2)
+    off = synth.segment_offsets(L)
+    total = int(off[-1])
+    x = synth.segment_matrix(synth.SEGMENTS.seed, total, cols, device=device)
+    cfg = loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"), [S, cols])
+    assert cfg["workgroups"][0] < S
+    out, tails = loom.segment_sums(x, off.to(device))
+    g, t = _np(out), _np(tails)
+    ref, rtails, _, _ = oracle.segment_sums(x.cpu().numpy(), off.numpy(), shadows=False)
+    assert np.array_equal(_bits(g), _bits(ref))
+    assert np.array_equal(t, rtails)
+
+
+def test_routed_combine_past_grid_limit(loom, device):
+    # 2^26 + 3 tokens: some waves take two tokens
+    tokens, routes, hidden, num_rows = 2**26 + 3, 1, 4, 1000
+    ids = synth.randint(92, 1, 0, tokens * routes, -1, num_rows).view(tokens, routes).to(torch.int32)
+    wts = synth.uniform_pm1(92, 2, 0, tokens * routes).view(tokens, routes)
+    pay = synth.normal(92, 3, 0, num_rows * hidden).view(num_rows, hidden)
+    cfg = loom.launch_config_invoke(loom.launch_config_lookup("routed_combine"), [tokens, routes, hidden])
+    assert cfg["workgroups"][0] < tokens
+    out = _np(loom.routed_combine(ids.to(device), wts.to(device), pay.to(device)))
+    ref, _, _ = oracle.routed_combine(ids.numpy(), wts.numpy(), pay.numpy(), shadows=False)
+    assert np.array_equal(_bits(out), _bits(ref))
+
+
+@pytest.mark.parametrize("rows,k", [(20_000_000, 256), (3_000_000, 1536), (2**24 + 100, 4096)])
+def test_i8_gemv_forms_past_4gib(loom, device, rows, k):
+    # one vector in each GEMV form over more than 4 GiB of weights: rows packed
+    # several to a record, a wave per block of rows, and a workgroup per row --
+    # the last with more rows than a grid of fewer than 2^32 work-items holds,
+    # so some workgroups take two rows
+    seed = synth.GEMV.seed
+    w = synth.i8_matrix(seed, synth.S_W, rows, k, device=device)
+    x = synth.i8_rows(seed, synth.S_X, 0, 1, k)
+    ws = synth.scales(seed, synth.S_WSCALE, 0, rows)
+    y, acc = loom.i8_dequant_dot(loom.pack_int8(w), ws.to(device), loom.pack_int8(x.to(device)), None,
+                                 want_acc=True)
+    gy, gacc = _np(y), _np(acc)
+    sample = _late_rows(rows, k, 40, seed=k)
+    sample = np.unique(np.concatenate([sample, np.arange(rows - 70, rows)]))
+    wsamp = torch.cat([synth.i8_rows(seed, synth.S_W, int(r), 1, k) for r in sample])
+    assert torch.equal(wsamp[-1].to(device), w[int(sample[-1])])
+    del w
+    ry, racc = oracle.i8_dequant_dot(wsamp.numpy(), ws.numpy()[sample], x.numpy(), None)
+    assert np.array_equal(gacc[sample], racc)
+    assert np.array_equal(_bits(gy[sample]), _bits(ry))

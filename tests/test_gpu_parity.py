@@ -9,8 +9,11 @@ Gates:
   * segment sums: bit-exact (each column is the same in-order f32 recurrence).
 
 Small cases span several tiles and ragged tails and are compared element by
-element; the full workload sizes are compared on outputs sampled at random
-(the oracle regenerates the sampled rows from the counter-based generator).
+element.  At the full workload sizes every output of the dense row sums and of
+both dequant-dot workloads is compared (the inputs generated on the GPU are
+copied to the host, after a regenerated sample has been checked equal to
+them); the segment sums, 34 GB of input, are compared on every segment of one
+sixteenth of the segments and on segments sampled from the rest.
 """
 import numpy as np
 import pytest
@@ -156,18 +159,14 @@ def test_row_sums_strided_poisoned(loom, device, rows, cols, stride, offset):
     assert_sum_close(g, ref, d, a, what="strided")
 
 
-def test_row_sums_full_size_sampled(loom, device):
+def test_row_sums_full_size(loom, device):
     rows, cols = 65536, 4096
     x = synth.dense_matrix(synth.DENSE.seed, rows, cols, device=device)
     g = _np(loom.row_sums(x))
-    rng = np.random.default_rng(0)
-    sample = np.unique(np.concatenate([[0, 7, 8, rows - 1], rng.integers(0, rows, 60)]))
-    xs = torch.cat([synth.dense_rows(synth.DENSE.seed, int(r), 1, cols) for r in sample])
-    assert torch.equal(xs[-1].to(device), x[int(sample[-1])])  # GPU input == regenerated rows
-    ref, d, a = oracle.row_sums(xs.numpy())
-    assert_sum_close(g[sample], ref, d, a, what="65536x4096 sampled")
-    # every row: the sum of a U[-1,1) row of 4096 is far below 4096 in magnitude
-    assert np.all(np.isfinite(g)) and np.all(np.abs(g) < 1024)
+    for r in (0, 7, 8, 40000, rows - 1):  # the GPU-generated input is the generator's
+        assert torch.equal(synth.dense_rows(synth.DENSE.seed, r, 1, cols)[0], x[r].cpu())
+    ref, d, a = oracle.row_sums(x.cpu().numpy())
+    assert_sum_close(g, ref, d, a, what="65536x4096, every row")
 
 
 # ------------------------------------------------------------------ segment sums
@@ -243,7 +242,7 @@ def test_segment_sums_bad_offsets_reported(loom, device):
     assert np.all(np.isnan(g[3]))  # [12, 12) lies beyond the 10 rows
 
 
-def test_segment_sums_full_size_sampled(loom, device):
+def test_segment_sums_full_size(loom, device):
     S, cols = 16384, 256
     L = synth.segment_lengths(synth.SEGMENTS.seed, S, 4096)
     off = synth.segment_offsets(L)
@@ -252,6 +251,13 @@ def test_segment_sums_full_size_sampled(loom, device):
     out, tails = loom.segment_sums(x, off.to(device))
     g, t = _np(out), _np(tails)
     assert np.array_equal(t, (L.numpy() % 8).astype(np.int32))
+    # every segment of one sixteenth (1024 consecutive segments, ~2 GB of rows)
+    s0, s1 = 5 * S // 16, 6 * S // 16
+    b, e = int(off[s0]), int(off[s1])
+    assert torch.equal(synth.segment_rows(synth.SEGMENTS.seed, b, 1, cols)[0], x[b].cpu())
+    ref, _, _, _ = oracle.segment_sums(x[b:e].cpu().numpy(), (off[s0:s1 + 1] - b).numpy())
+    assert np.array_equal(g[s0:s1].view(np.uint32), ref.view(np.uint32))
+    # and segments sampled from the rest, their rows regenerated on the host
     rng = np.random.default_rng(1)
     longest = int(L.argmax())
     sample = np.unique(np.concatenate([[0, S - 1, longest], np.flatnonzero(L.numpy() == 0)[:2],
@@ -289,11 +295,18 @@ def _check_i8(gy, gacc, w, x, ws, xs, what):
 
 
 I8_CASES = [
-    # (rows, k, batch) -- batch 1 runs v_dot4, batch >= 2 the MFMA kernel
-    # (one vector with k a multiple of 1024 or k >= 12288 runs the GEMV, any
-    # other k the matrix-core tile kernel)
-    (1, 4, 1), (7, 4, 1), (8, 1024, 1), (9, 1028, 1), (17, 8192, 1), (33, 1040, 1), (100, 2112, 1), (5, 0, 1),
-    (3000, 1536, 1), (40, 12804, 1), (70, 3072, 1),
+    # (rows, k, batch) -- batch 1 runs a v_dot4 GEMV, batch >= 2 an MFMA kernel.
+    # One vector, rows of up to 512 bytes packed several to a record (1 to 32
+    # lanes per row; a wave per 64 rows; groups partly past the row):
+    (1, 4, 1), (7, 4, 1), (5, 0, 1), (100, 8, 1), (65, 16, 1), (130, 20, 1), (64, 64, 1), (200, 100, 1),
+    (129, 252, 1), (1000, 256, 1), (77, 260, 1), (300, 508, 1), (4097, 512, 1),
+    # rows of 513 bytes to 4 KiB, a wave per block of rows (whole and partly
+    # filled last records, blocks that end mid-matrix):
+    (3, 516, 1), (8, 1024, 1), (9, 1028, 1), (33, 1040, 1), (100, 2112, 1), (3000, 1536, 1), (70, 3072, 1),
+    (41, 4092, 1),
+    # rows of 4 KiB or more, a workgroup per row (waves with no record at
+    # all, a partial last record):
+    (17, 8192, 1), (40, 12804, 1), (13, 4096, 1), (19, 4100, 1), (23, 5124, 1), (6, 16896, 1),
     (3, 64, 2), (15, 256, 3), (16, 260, 8), (17, 1000, 8), (100, 8192, 8), (33, 64, 16), (40, 512, 17),
     (20, 1024, 32), (18, 320, 33), (16, 4096, 64), (1, 4, 2), (31, 8, 5),
     # the tile kernel's k split: 1 wave per tile (k <= 2048, several records),
@@ -327,12 +340,14 @@ def test_i8_dequant_dot(loom, device, rows, k, batch):
     _check_i8(gy, gacc, w, x, ws, xs, f"{rows}x{k}x{batch}")
 
 
-@pytest.mark.parametrize("batch", [8, 16, 33])
-def test_i8_unaligned_operands(loom, device, batch):
+@pytest.mark.parametrize("rows,k,batch", [(70, 4096, 8), (70, 4096, 16), (70, 4096, 33), (70, 4096, 1),
+                                           (70, 5000, 1), (70, 1536, 1), (70, 1028, 1), (130, 100, 1),
+                                           (130, 12, 1)])
+def test_i8_unaligned_operands(loom, device, rows, k, batch):
     # weights and vectors starting 4 bytes past a 16-byte boundary: the kernels
-    # read them as single words instead of 16-byte groups
-    rows, k = 70, 4096
-    w, x, ws, xs = _i8_case(77 + batch, rows, k, batch)
+    # read them as single words instead of 16-byte groups (for one vector in
+    # each GEMV form)
+    w, x, ws, xs = _i8_case(77 + batch + k, rows, k, batch)
     wbuf = torch.zeros(rows * k // 4 + 1, dtype=torch.int32, device=device)
     xbuf = torch.zeros(batch * k // 4 + 1, dtype=torch.int32, device=device)
     wp = wbuf[1:].view(rows, k // 4)
@@ -391,18 +406,31 @@ def _i8_full(loom, device, wl, rows, k, batch):
     wscpu = synth.scales(seed, synth.S_WSCALE, 0, rows)[torch.from_numpy(sample)]
     xscpu = synth.scales(seed, synth.S_XSCALE, 0, batch) if batch > 1 else None
     _check_i8(gy[sample], gacc[sample], wsamp, xcpu, wscpu, xscpu, f"{rows}x{k}x{batch} sampled")
+    # every output, against the oracle over row blocks on the host cores (each
+    # output's arithmetic is the single-threaded oracle's)
+    from concurrent.futures import ThreadPoolExecutor
+    hw, hx, hws = w.cpu().numpy(), x.cpu().numpy(), ws.cpu().numpy()
+    hxs = None if xs is None else xs.cpu().numpy()
+    blocks = [(a, min(rows, a + 2048)) for a in range(0, rows, 2048)]
+    with ThreadPoolExecutor(min(16, len(blocks))) as pool:
+        parts = list(pool.map(lambda ab: oracle.i8_dequant_dot(hw[ab[0]:ab[1]], hws[ab[0]:ab[1]], hx, hxs), blocks))
+    ry = np.concatenate([p[0] for p in parts])
+    racc = np.concatenate([p[1] for p in parts])
+    assert np.array_equal(gacc, racc.reshape(gacc.shape)), f"{rows}x{k}x{batch}: acc mismatch"
+    err = np.abs(gy.astype(np.float64) - ry.reshape(gy.shape))
+    assert np.all(err <= REL_DQ * np.abs(ry.reshape(gy.shape))), f"{rows}x{k}x{batch}: max err {err.max()}"
 
 
-def test_i8_gemv_full_size_sampled(loom, device):
+def test_i8_gemv_full_size(loom, device):
     _i8_full(loom, device, synth.GEMV, 16384, 8192, 1)
 
 
-def test_i8_batched_full_size_sampled(loom, device):
+def test_i8_batched_full_size(loom, device):
     _i8_full(loom, device, synth.BATCHED, 28672, 8192, 8)
 
 
 @pytest.mark.parametrize("rows,k", [(28672, 8192), (57344, 4096)])
-def test_i8_batched_64_full_size_sampled(loom, device, rows, k):
+def test_i8_batched_64_full_size(loom, device, rows, k):
     # the column-tile kernel at full size: one (7 row tiles per wave) and two
     # workgroups per CU
     _i8_full(loom, device, synth.BATCHED, rows, k, 64)
@@ -587,3 +615,35 @@ def test_binding_rejects_short_buffers(loom, device):
         loom.sum_guarded_rows(torch.zeros(4, 32, 4, device=device), 4, 4, 32, out=torch.empty(31, device=device))
     with pytest.raises(ValueError):
         loom.copy_f32(torch.zeros(10, device=device), out=torch.empty(9, device=device))
+
+
+# ------------------------------------------------------------------ launch status
+
+def _loaded_hip_runtime():
+    """The HIP runtime this process (torch and libloom.so) uses, found among the
+    mapped libraries, so the call below reaches the same runtime state."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64.so" in line}
+    assert len(paths) == 1, paths
+    return ctypes.CDLL(paths.pop())
+
+
+def test_stale_hip_error_is_not_reported(loom, device):
+    # An unrelated HIP call that fails first (an invalid device index) leaves
+    # its error as the thread's last error; a valid call must still report
+    # LOOM_OK, and the same launch on the real device must compute.
+    # (no torch call between the failing call and the library's: torch would
+    # itself pick up the stale error)
+    import ctypes
+    hip = _loaded_hip_runtime()
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    x = torch.ones(40, 300, device=device)
+    out = torch.empty(40, device=device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(100000) != 0  # hipErrorInvalidDevice, current device unchanged
+    st = loom.library().loom_row_sums(ctypes.c_void_p(x.data_ptr()), 40, 300, 300, ctypes.c_void_p(out.data_ptr()),
+                                      stream)
+    assert st == loom.OK
+    assert np.all(_np(out) == 300.0)
