@@ -64,9 +64,9 @@ constexpr int kI8ColsDepth = LOOM_I8_COLS_DEPTH;
 // (weights), so the load is non-temporal; activations are reused and cached.
 // SELECT: the guards are selects, not branches -- a word past the row is
 // loaded from the row's first word (kw > 0 whenever a group is read) and
-// replaced by zero -- so every lane issues the same loads and a GEMV's
-// read-ahead keeps its partial waits across a partly filled last record; the
-// matrix-core kernels keep the branches, which need fewer registers.
+// replaced by zero -- so every lane issues the same loads and the read-ahead
+// keeps its partial waits where many records are partly filled (the packed
+// GEMV forms); elsewhere the branches, which need fewer registers, serve.
 template <bool FULL, bool VEC16, bool STREAM, bool SELECT = false>
 __device__ __forceinline__ int4v load_words(const int32_t *__restrict__ row, int c, int kw) {
     if constexpr (SELECT && VEC16) {
@@ -111,11 +111,10 @@ __device__ __forceinline__ int dot16(int4v a, int4v b, int acc) {
 }
 
 // ----------------------------------------------------------------------------
-// One vector, rows of 513 bytes to 4 KiB (gemv_form).  One wave owns a block
+// One vector, rows of whole 1 KiB records and long rows (gemv_form).  One wave owns a block
 // of consecutive rows -- gemv_rows_per_wave(k), about 8 KiB of weights --
 // which is one contiguous stretch of the weight matrix, and walks it row after
-// row.  A record is one 1 KiB column block of one row (the last one of a row
-// guarded when k is not a multiple of 1024) plus
+// row.  A record is one 1 KiB column block of one row plus
 // the activation group each lane needs at the same columns (16 bytes, reused
 // by every wave and kept in the caches), so the read-ahead runs across row
 // boundaries and the wave's weights stream in address order.  At the end of
@@ -128,7 +127,9 @@ struct GemvRecord {
     int4v xv, wv;
 };
 
-// ONE_ROW: rows_per_wave == 1, known at compile time.
+// ONE_ROW: rows_per_wave == 1, known at compile time.  FULL: rows of whole
+// 1 KiB records; otherwise each row's last record is guarded (this form takes
+// such rows only from 12 KiB, one row per wave).
 template <bool FULL, bool VEC16, int DEPTH, bool ONE_ROW>
 __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restrict__ w, const float *__restrict__ w_scale,
                                                         const int32_t *__restrict__ x,
@@ -155,8 +156,8 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
         [&]() {
             GemvRecord q;
             const int c = lcol + lane * 4;
-            q.xv = load_words<FULL, VEC16, false, true>(x, c, kw);
-            q.wv = load_words<FULL, VEC16, true, true>(wrow, c, kw);
+            q.xv = load_words<FULL, VEC16, false>(x, c, kw);
+            q.wv = load_words<FULL, VEC16, true>(wrow, c, kw);
             if (lcol >= kw - kBlockWords) {
                 lcol = 0;
                 wrow += kw;
@@ -187,29 +188,30 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
 }
 
 // ----------------------------------------------------------------------------
-// One vector, long rows (gemv_form: k of 4 KiB or more): one workgroup of
-// kGemvWideWaves waves per row.  Wave w streams a contiguous share of the
-// row's 1 KiB records (a partly filled last record is guarded), folds them
-// with v_dot4 into per-lane int32 partials, reduces them across the wave, and
-// the wave totals are added in wave order (exact).  Every wave of the launch
-// reads a short contiguous stretch of one row with all of its loads issued
-// almost at once, which is what the HBM stream favours: at 16384 x 8192 this
-// took 19.9 us against 20.2 us for a wave per row.  Past the work-item limit
-// of a grid, each workgroup takes every grid.x-th row.
+// One vector, long rows of whole 1 KiB records (gemv_form): one workgroup per
+// row, of gemv_wide_waves(k) waves -- about LOOM_GEMV_WIDE_RECORDS records
+// each, at most kGemvWideMaxWaves.  Wave w streams a contiguous share of the
+// row's records, folds them with v_dot4 into per-lane int32 partials,
+// reduces them across the wave, and the wave totals are added in wave order
+// (exact).  Every wave of the launch reads a short contiguous stretch of one
+// row with all of its loads issued almost at once, which is what the HBM
+// stream favours.  Past the work-item limit of a grid, each workgroup takes
+// every grid.x-th row.
 // ----------------------------------------------------------------------------
 template <bool FULL, bool VEC16, int DEPTH>
-__global__ __launch_bounds__(kWave * kGemvWideWaves) void i8_gemv_wide_kernel(
+__global__ __launch_bounds__(kWave * kGemvWideMaxWaves) void i8_gemv_wide_kernel(
     const int32_t *__restrict__ w, const float *__restrict__ w_scale, const int32_t *__restrict__ x,
     const float *__restrict__ x_scale, int rows, int kw, float *__restrict__ out, int32_t *__restrict__ acc_out) {
+    static_assert(FULL, "rows of whole 1 KiB records");
     constexpr int kBlockWords = kWave * 4;
-    constexpr int W = kGemvWideWaves;
     const int lane = lane_id();
+    const int waves = blockDim.x / kWave;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int records = kw / kBlockWords + (kw % kBlockWords != 0);
-    const int per = (records + W - 1) / W;
+    const int per = (records + waves - 1) / waves;
     const int first = min(records, wave * per);
     const int n = min(records, first + per) - first;
-    __shared__ int part[W];
+    __shared__ int part[kGemvWideMaxWaves];
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
         const int32_t *wrow = w + row * kw;
         int lcol = first * kBlockWords;
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kWave * kGemvWideWaves) void i8_gemv_wide_kernel(
         __syncthreads();
         if (threadIdx.x == 0) {
             int sum = 0;
-            for (int v = 0; v < W; ++v) sum += part[v];
+            for (int v = 0; v < waves; ++v) sum += part[v];
             float y = (float)sum;
             y = y * w_scale[row];
             if (x_scale) y = y * x_scale[0];
@@ -242,6 +244,80 @@ __global__ __launch_bounds__(kWave * kGemvWideWaves) void i8_gemv_wide_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// One vector, rows longer than 512 bytes that are not whole 1 KiB records
+// but whole 256-byte (LOG2L = 4) or 512-byte (LOG2L = 5) pieces -- the
+// grouped form (gemv_group_log2_lanes): a record puts R = 64 / L rows side by
+// side, L = 2^LOG2L lanes and 16 L bytes per row (lane l: row l / L of the
+// group, 16-byte group l mod L of the piece), so no record is partly empty
+// where a 1 KiB record per row would be; a load instruction reads R rows x
+// 16 L contiguous bytes.  The wave owns rows_per_wave consecutive rows (a
+// multiple of R, at most 64) and walks them group by group, each group's
+// pieces in k order, with the read-ahead running across groups.  At the end
+// of a group the first LOG2L steps of the wave reduction sum each row's L
+// lanes (exact int32) and a lane permute hands row i of the wave its total in
+// lane i.  Rows past the matrix load the wave's first row and drop the value.
+// ----------------------------------------------------------------------------
+template <bool VEC16, int LOG2L, int DEPTH>
+__global__ __launch_bounds__(kWave) void i8_gemv_grouped_kernel(const int32_t *__restrict__ w,
+                                                                const float *__restrict__ w_scale,
+                                                                const int32_t *__restrict__ x,
+                                                                const float *__restrict__ x_scale, int rows, int kw,
+                                                                int rows_per_wave, float *__restrict__ out,
+                                                                int32_t *__restrict__ acc_out) {
+    static_assert(LOG2L >= 1 && LOG2L <= 5, "2 to 32 lanes per row");
+    constexpr int L = 1 << LOG2L;
+    constexpr int R = kWave / L;
+    constexpr int kPieceWords = 4 * L;
+    const int lane = lane_id();
+    const int sub = lane >> LOG2L;          // row within the group
+    const int q4 = (lane & (L - 1)) * 4;    // the lane's first word within the piece
+    const int row0 = blockIdx.x * rows_per_wave;
+    const int left = min(rows_per_wave, rows - row0);  // rows of this wave (> 0)
+    const int pieces = kw / kPieceWords + (kw % kPieceWords != 0);
+    const int groups = (left + R - 1) / R;
+    const int32_t *first = w + (int64_t)row0 * kw;
+    // producer: group lg, piece lp; consumer: group cg, piece cp
+    int lg = 0, lp = 0, cg = 0, cp = 0, acc = 0, mine = 0;
+    const int32_t *lrow = first + (int64_t)(sub < left ? sub : 0) * kw;
+    pipelined<DEPTH, GemvRecord>(
+        groups * pieces,
+        [&]() {
+            GemvRecord q;
+            const int c = lp * kPieceWords + q4;
+            q.wv = load_words<false, VEC16, true, true>(lrow, c, kw);
+            q.xv = load_words<false, VEC16, false, true>(x, c, kw);
+            if (++lp == pieces) {
+                lp = 0;
+                ++lg;
+                const int r = lg * R + sub;
+                lrow = first + (int64_t)(r < left ? r : 0) * kw;
+            }
+            return q;
+        },
+        [&](const GemvRecord &q) {
+            acc = dot16(q.wv, q.xv, acc);
+            if (++cp == pieces) {
+                const int total = group_sum<LOG2L>(acc);
+                // lane cg * R + i takes the total of row i of the group (held by lane i * L)
+                const int i = lane - cg * R;
+                const int got = __builtin_amdgcn_ds_bpermute(((i >= 0 && i < R) ? i * L : 0) * 4, total);
+                if (i >= 0 && i < R) mine = got;
+                acc = 0;
+                cp = 0;
+                ++cg;
+            }
+        });
+    if (lane < left) {
+        const int row = row0 + lane;
+        float y = (float)mine;
+        y = y * w_scale[row];
+        if (x_scale) y = y * x_scale[0];
+        out[row] = y;
+        if (acc_out) acc_out[row] = mine;
+    }
+}
+
+// ----------------------------------------------------------------------------
 // One vector, short rows (gemv_form: k <= 512): several rows per 1 KiB
 // record, as the narrow row sums pack them.  A record holds R = 64 / L rows
 // side by side, L = 2^LOG2L the smallest power of two with 16 L >= k bytes:
@@ -249,25 +325,26 @@ __global__ __launch_bounds__(kWave * kGemvWideWaves) void i8_gemv_wide_kernel(
 // activation group is the same for every row, so it is loaded once.  Each
 // lane folds its group with v_dot4, the first LOG2L steps of the wave
 // reduction sum each aligned group of L lanes (exact int32), and a lane
-// permute hands row i of the wave its total in lane i.  A wave owns 64
-// consecutive rows (L records); lanes past the last row load the wave's first
-// row and drop the value, so every record issues the same loads.
+// permute hands row i of the wave its total in lane i.  A wave owns
+// rows_per_wave consecutive rows (whole records of about 8 KiB together, at
+// most 64 rows); lanes past the last row load the wave's first row and drop
+// the value, so every record issues the same loads.
 // ----------------------------------------------------------------------------
 template <bool VEC16, int LOG2L, int DEPTH>
 __global__ __launch_bounds__(kWave) void i8_gemv_narrow_kernel(const int32_t *__restrict__ w,
                                                                const float *__restrict__ w_scale,
                                                                const int32_t *__restrict__ x,
                                                                const float *__restrict__ x_scale, int rows, int kw,
-                                                               float *__restrict__ out,
+                                                               int rows_per_wave, float *__restrict__ out,
                                                                int32_t *__restrict__ acc_out) {
     constexpr int L = 1 << LOG2L;
     constexpr int R = kWave / L;
     const int lane = lane_id();
     const int sub = lane >> LOG2L;  // row within the record
     const int c = (lane & (L - 1)) * 4;  // first word of the lane's group
-    const int row0 = blockIdx.x * kWave;
-    const int left = rows - row0;  // rows of this wave that exist (> 0)
-    const int nrec = kw > 0 ? min(L, (left + R - 1) / R) : 0;
+    const int row0 = blockIdx.x * rows_per_wave;
+    const int left = min(rows_per_wave, rows - row0);  // rows of this wave that exist (> 0)
+    const int nrec = kw > 0 ? (left + R - 1) / R : 0;
     const int4v xv = nrec > 0 ? load_words<false, VEC16, false, true>(x, c, kw) : int4v{0, 0, 0, 0};
     const int32_t *first = w + (int64_t)row0 * kw;
     int lrec = 0, crec = 0, mine = 0;
@@ -717,11 +794,12 @@ static bool launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t
 template <bool VEC16>
 static void launch_gemv_narrow(dim3 grid, dim3 block, hipStream_t stream, const int32_t *w, const float *w_scale,
                                const int32_t *x, const float *x_scale, int rows, int kw, float *out, int32_t *acc) {
+    const int rpw = gemv_narrow_rows_per_wave(4 * (int64_t)kw);
     switch (gemv_narrow_log2_lanes(kw)) {
 #define LOOM_NARROW_CASE(L2)                                                                                     \
     case L2:                                                                                                     \
         i8_gemv_narrow_kernel<VEC16, L2, kGemvNarrowDepth>                                                       \
-            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, out, acc);                           \
+            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, rpw, out, acc);                      \
         break;
         LOOM_NARROW_CASE(0) LOOM_NARROW_CASE(1) LOOM_NARROW_CASE(2) LOOM_NARROW_CASE(3) LOOM_NARROW_CASE(4)
         default:
@@ -748,7 +826,6 @@ hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w
         default: break;
     }
     if (i8_use_gemv(4 * (int64_t)k_words, batch)) {
-        const bool full = k_words % (kWave * 4) == 0;
         switch (gemv_form(4 * (int64_t)k_words)) {
             case kGemvNarrow:
                 if (vec16)
@@ -756,24 +833,44 @@ hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w
                 else
                     launch_gemv_narrow<false>(grid, block, stream, w, w_scale, x, x_scale, rows, k_words, out, acc);
                 break;
+            case kGemvGrouped: {
+                const int rpw = gemv_group_rows_per_wave(4 * (int64_t)k_words);
+                if (gemv_group_log2_lanes(4 * (int64_t)k_words) == 5) {
+                    if (vec16)
+                        i8_gemv_grouped_kernel<true, 5, kGemvDepth><<<grid, block, 0, stream>>>(
+                            w, w_scale, x, x_scale, rows, k_words, rpw, out, acc);
+                    else
+                        i8_gemv_grouped_kernel<false, 5, kGemvDepth><<<grid, block, 0, stream>>>(
+                            w, w_scale, x, x_scale, rows, k_words, rpw, out, acc);
+                } else {
+                    if (vec16)
+                        i8_gemv_grouped_kernel<true, 4, kGemvDepth><<<grid, block, 0, stream>>>(
+                            w, w_scale, x, x_scale, rows, k_words, rpw, out, acc);
+                    else
+                        i8_gemv_grouped_kernel<false, 4, kGemvDepth><<<grid, block, 0, stream>>>(
+                            w, w_scale, x, x_scale, rows, k_words, rpw, out, acc);
+                }
+                break;
+            }
             case kGemvWide:
-                if (full && vec16)
+                if (vec16)
                     i8_gemv_wide_kernel<true, true, kGemvWideDepth><<<grid, block, 0, stream>>>(
                         w, w_scale, x, x_scale, rows, k_words, out, acc);
-                else if (vec16)
-                    i8_gemv_wide_kernel<false, true, kGemvWideDepth><<<grid, block, 0, stream>>>(
-                        w, w_scale, x, x_scale, rows, k_words, out, acc);
                 else
-                    i8_gemv_wide_kernel<false, false, kGemvWideDepth><<<grid, block, 0, stream>>>(
+                    i8_gemv_wide_kernel<true, false, kGemvWideDepth><<<grid, block, 0, stream>>>(
                         w, w_scale, x, x_scale, rows, k_words, out, acc);
                 break;
             default: {
                 const int rpw = gemv_rows_per_wave(k_words);
+                const bool full = k_words % (kWave * 4) == 0;
                 if (full && vec16 && rpw == 1)
                     i8_gemv_kernel<true, true, kGemvDepth, true><<<grid, block, 0, stream>>>(
                         w, w_scale, x, x_scale, rows, k_words, rpw, out, acc);
                 else if (full && vec16)
                     i8_gemv_kernel<true, true, kGemvDepth, false><<<grid, block, 0, stream>>>(
+                        w, w_scale, x, x_scale, rows, k_words, rpw, out, acc);
+                else if (full)
+                    i8_gemv_kernel<true, false, kGemvDepth, false><<<grid, block, 0, stream>>>(
                         w, w_scale, x, x_scale, rows, k_words, rpw, out, acc);
                 else if (vec16)
                     i8_gemv_kernel<false, true, kGemvDepth, false><<<grid, block, 0, stream>>>(

@@ -84,45 +84,97 @@ constexpr int row_sums_waves_per_row(int64_t cols) {
 constexpr int kSegmentBlockCols = 256;
 
 // Blocking of the int8 kernels.  One vector always runs a v_dot4 GEMV, in
-// one of three forms by row length k (bytes):
-//   narrow  k <= LOOM_GEMV_NARROW_MAX_K: several rows packed into each 1 KiB
-//           record, a wave per 64 rows;
-//   rows    up to LOOM_GEMV_WIDE_MIN_K: a wave per gemv_rows_per_wave(k)
-//           consecutive rows (about 8 KiB), each row one or more 1 KiB records;
-//   wide    longer rows: a workgroup of kGemvWideWaves waves per row.
+// one of four forms by row length k (bytes):
+//   narrow   k <= LOOM_GEMV_NARROW_MAX_K: several rows packed into each 1 KiB
+//            record, a wave per gemv_narrow_rows_per_wave(k) rows;
+//   grouped  other k below LOOM_GEMV_GROUPED_MAX_K that is not a multiple of
+//            1024: records of 2 rows x 512 B (k a multiple of 512) or 4 rows x
+//            256 B, so that the pieces of a row fill its records, a wave per
+//            gemv_group_rows_per_wave(k) rows;
+//   rows     any other k: a wave per gemv_rows_per_wave(k) consecutive rows
+//            (about 8 KiB), read row by row in 1 KiB records (the last one of
+//            a row partly filled when k is not a multiple of 1024: a small
+//            share of such long rows);
+//   wide     k a multiple of 1024 from LOOM_GEMV_WIDE_MIN_K to
+//            LOOM_GEMV_WIDE_MAX_K: a workgroup per row of gemv_wide_waves(k)
+//            waves.
+// Over 128 MiB of weights (one MI355X, back-to-back launches) each form was
+// kept where it measured fastest: rows of 768 to 8704 bytes that are not whole
+// 1 KiB records took 21.0-23.0 us grouped against 23.1-24.5 us in 1 KiB
+// records per row or on the matrix cores; from 12288 bytes the partly filled
+// record costs less than pairs of 512-byte pieces (k = 12800: 23.5 against
+// 23.9 us); a workgroup per row won only at 6-8 KiB rows (k = 6144:
+// 20.5 against 20.9 us; k = 4096: 22.2 against 20.7; k = 10240: 22.0 against
+// 21.1).
 // Several vectors run an int8 MFMA kernel: one 16-row matrix-core tile per
 // workgroup, whose KSPLIT waves split the k range and combine their int32
 // partials through LDS in wave order (exact).  Tuning builds may override the
 // macros.
 #ifndef LOOM_GEMV_WAVE_BYTES
-#define LOOM_GEMV_WAVE_BYTES 8192  // rows form: about 8 KiB of weights per wave
+#define LOOM_GEMV_WAVE_BYTES 8192  // rows and grouped forms: about 8 KiB of weights per wave
 #endif
 #ifndef LOOM_GEMV_NARROW_MAX_K
 #define LOOM_GEMV_NARROW_MAX_K 512
 #endif
-#ifndef LOOM_GEMV_WIDE_MIN_K
-#define LOOM_GEMV_WIDE_MIN_K 4096
+#ifndef LOOM_GEMV_GROUPED_MAX_K
+#define LOOM_GEMV_GROUPED_MAX_K 12288
 #endif
-constexpr int kGemvWideWaves = 4;
-enum GemvForm : int { kGemvNarrow = 0, kGemvRows = 1, kGemvWide = 2 };
+#ifndef LOOM_GEMV_WIDE_MIN_K
+#define LOOM_GEMV_WIDE_MIN_K 6144
+#endif
+#ifndef LOOM_GEMV_WIDE_MAX_K
+#define LOOM_GEMV_WIDE_MAX_K 8192
+#endif
+#ifndef LOOM_GEMV_WIDE_RECORDS
+#define LOOM_GEMV_WIDE_RECORDS 2  // 1 KiB records per wave of the wide form
+#endif
+constexpr int kGemvWideMaxWaves = 16;
+enum GemvForm : int { kGemvNarrow = 0, kGemvRows = 1, kGemvWide = 2, kGemvGrouped = 3 };
 constexpr GemvForm gemv_form(int64_t k) {
 #ifdef LOOM_GEMV_FORCE_FORM
-    if (LOOM_GEMV_FORCE_FORM >= 0 && (LOOM_GEMV_FORCE_FORM != kGemvNarrow || k <= 512))
+    if (LOOM_GEMV_FORCE_FORM >= 0 && k > LOOM_GEMV_NARROW_MAX_K &&
+        (LOOM_GEMV_FORCE_FORM == kGemvGrouped || k % 1024 == 0))
         return (GemvForm)LOOM_GEMV_FORCE_FORM;
 #endif
-    return k <= LOOM_GEMV_NARROW_MAX_K ? kGemvNarrow : k < LOOM_GEMV_WIDE_MIN_K ? kGemvRows : kGemvWide;
+    return k <= LOOM_GEMV_NARROW_MAX_K                                                  ? kGemvNarrow
+           : k % 1024 != 0 && k < LOOM_GEMV_GROUPED_MAX_K                               ? kGemvGrouped
+           : k % 1024 == 0 && k >= LOOM_GEMV_WIDE_MIN_K && k <= LOOM_GEMV_WIDE_MAX_K ? kGemvWide
+                                                                                        : kGemvRows;
+}
+constexpr int gemv_wide_waves(int64_t k) {
+    const int64_t records = (k + 1023) / 1024;
+    const int64_t wv = (records + LOOM_GEMV_WIDE_RECORDS - 1) / LOOM_GEMV_WIDE_RECORDS;
+    return wv < 1 ? 1 : wv > kGemvWideMaxWaves ? kGemvWideMaxWaves : (int)wv;
 }
 constexpr bool i8_use_gemv(int64_t k, int64_t batch) { return batch == 1 && k >= 0; }
+// grouped form: log2 of the lanes per row (32 when k is a multiple of 512,
+// else 16) and the rows of a wave, whole groups of 64 / L rows of about
+// LOOM_GEMV_WAVE_BYTES together, at most 64
+constexpr int gemv_group_log2_lanes(int64_t k) { return k % 512 == 0 ? 5 : 4; }
+constexpr int gemv_group_rows_per_wave(int64_t k) {
+    const int64_t r = int64_t(64) >> gemv_group_log2_lanes(k);
+    int64_t g = k > 0 ? LOOM_GEMV_WAVE_BYTES / (r * k) : 1;
+    g = g < 1 ? 1 : g > 64 / r ? 64 / r : g;
+    return (int)(g * r);
+}
 constexpr int gemv_rows_per_wave(int64_t k_words) {
     const int64_t r = k_words > 0 ? LOOM_GEMV_WAVE_BYTES / (4 * k_words) : 64;
     return r < 1 ? 1 : r > 64 ? 64 : (int)r;
 }
 // narrow form: log2 of the lanes per row, the smallest L with 4 L >= k_words
-// (at most 32 lanes, so at least two rows per record)
+// (at most 32 lanes, so at least two rows per record), and the rows of a
+// wave: whole records (64 / L rows each) of about LOOM_GEMV_WAVE_BYTES, at
+// most 64 rows
 constexpr int gemv_narrow_log2_lanes(int64_t k_words) {
     int l = 0;
     while ((int64_t(4) << l) < k_words) ++l;
     return l;
+}
+constexpr int gemv_narrow_rows_per_wave(int64_t k) {
+    const int64_t r = int64_t(64) >> gemv_narrow_log2_lanes(k / 4);
+    const int64_t rec = k > 0 ? LOOM_GEMV_WAVE_BYTES / (r * k) : 64;
+    const int64_t rows = r * (rec < 1 ? 1 : rec);
+    return rows > 64 ? 64 : (int)rows;
 }
 // Waves per 16-row tile of the tile kernel, each taking a contiguous 1/KS of
 // k: about 2 KiB of every row per wave.  Over ~224 MiB of weights with 2 and

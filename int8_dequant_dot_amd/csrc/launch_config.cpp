@@ -78,8 +78,9 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 }
 
 // i8_dequant_dot(rows, k, batch): for one vector, by gemv_form(k), one wave
-// per 64 short rows, one wave per block of gemv_rows_per_wave(k) rows, or one
-// workgroup of kGemvWideWaves waves per long row; for 9 to 16 vectors and k a multiple of 1024
+// per gemv_narrow_rows_per_wave(k), gemv_group_rows_per_wave(k) or
+// gemv_rows_per_wave(k) rows, or one workgroup of gemv_wide_waves(k) waves per
+// long row; for 9 to 16 vectors and k a multiple of 1024
 // from 4096 to 8192, one 16-wave workgroup per CU (at most one per 16-row
 // tile) that walks the tiles; for more than 16 vectors, one workgroup per
 // i8_cols_tile_rows rows with one wave per 16-vector column tile (LDS: two
@@ -90,11 +91,13 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
     if (i8_use_gemv(w[1], w[2])) {
         switch (gemv_form(w[1])) {
-            case kGemvNarrow: return set(c, ceil_div(w[0], kSubgroupSize), kSubgroupSize, 0);
+            case kGemvNarrow: return set(c, ceil_div(w[0], gemv_narrow_rows_per_wave(w[1])), kSubgroupSize, 0);
             case kGemvRows: return set(c, ceil_div(w[0], gemv_rows_per_wave(w[1] / 4)), kSubgroupSize, 0);
-            default:  // LDS: the wave totals
-                return set(c, grid_stride_groups(w[0], kSubgroupSize * kGemvWideWaves),
-                           kSubgroupSize * kGemvWideWaves, 4 * kGemvWideWaves);
+            case kGemvGrouped: return set(c, ceil_div(w[0], gemv_group_rows_per_wave(w[1])), kSubgroupSize, 0);
+            default: {  // LDS: the wave totals
+                const int64_t size = kSubgroupSize * gemv_wide_waves(w[1]);
+                return set(c, grid_stride_groups(w[0], size), (uint32_t)size, 4 * kGemvWideMaxWaves);
+            }
         }
     }
     if (const int chunks = i8_rows_chunks(w[0], w[1], w[2])) {

@@ -105,21 +105,30 @@ def test_launch_config_tiles(loom):
     assert loom.launch_config_invoke(seg, [100, 1000])["workgroups"] == (100, 4, 1)  # a wave per 256 columns
     assert loom.launch_config_invoke(seg, [5, 0])["workgroups"] == (5, 1, 1)  # still writes the tail counts
     i8 = loom.launch_config_lookup("i8_dequant_dot")
-    # one vector, always a v_dot4 GEMV: rows of 4 KiB or more a 4-wave
-    # workgroup per row (LDS: the 4 wave totals) ...
-    for k in (4096, 4100, 8192, 8704, 12804, 131068):
+    # one vector, always a v_dot4 GEMV: rows of 6 to 8 whole 1 KiB records a
+    # workgroup per row with a wave per 2 records (LDS: the wave totals) ...
+    for k, waves in ((6144, 3), (7168, 4), (8192, 4)):
         cfg = loom.launch_config_invoke(i8, [100, k, 1])
-        assert cfg["workgroups"] == (100, 1, 1) and cfg["workgroup_size"] == (256, 1, 1), k
-        assert cfg["workgroup_storage_bytes"] == 16, k
+        assert cfg["workgroups"] == (100, 1, 1) and cfg["workgroup_size"] == (64 * waves, 1, 1), k
+        assert cfg["workgroup_storage_bytes"] == 64, k
     assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 16384
-    # ... rows of 513 bytes to 4 KiB a wave per block of about 8 KiB of rows ...
-    for k, rows_per_wave in ((516, 15), (1024, 8), (1028, 7), (1536, 5), (2560, 3), (4092, 2)):
+    # ... other rows of whole 1 KiB records, and rows of 12 KiB or more, a wave
+    # per block of about 8 KiB of rows (at least one row) ...
+    for k, rows_per_wave in ((1024, 8), (2048, 4), (3072, 2), (4096, 2), (5120, 1), (9216, 1), (16384, 1),
+                             (130048, 1), (12292, 1), (12804, 1), (16896, 1), (131068, 1)):
         cfg = loom.launch_config_invoke(i8, [100, k, 1])
         assert cfg["workgroups"] == (-(-100 // rows_per_wave), 1, 1) and cfg["workgroup_size"] == (64, 1, 1), k
-    # ... and rows of up to 512 bytes a wave per 64 rows, several rows per record
-    for k in (0, 4, 16, 100, 256, 512):
+    # ... other rows longer than 512 bytes in groups of 2 rows x 512 B pieces (k
+    # a multiple of 512) or 4 rows x 256 B, whole groups of about 8 KiB a wave ...
+    for k, rows_per_wave in ((516, 12), (528, 12), (768, 8), (1028, 4), (1040, 4), (1280, 4), (1536, 4),
+                             (2560, 2), (4092, 4), (4100, 4), (8704, 2), (12284, 4)):
         cfg = loom.launch_config_invoke(i8, [100, k, 1])
-        assert cfg["workgroups"] == (2, 1, 1) and cfg["workgroup_size"] == (64, 1, 1), k
+        assert cfg["workgroups"] == (-(-100 // rows_per_wave), 1, 1) and cfg["workgroup_size"] == (64, 1, 1), k
+    # ... and rows of up to 512 bytes packed 64 / L to a record (16 L >= k),
+    # whole records of about 8 KiB a wave, at most 64 rows
+    for k, rows_per_wave in ((0, 64), (4, 64), (16, 64), (100, 64), (256, 32), (260, 30), (512, 16)):
+        cfg = loom.launch_config_invoke(i8, [1000, k, 1])
+        assert cfg["workgroups"] == (-(-1000 // rows_per_wave), 1, 1) and cfg["workgroup_size"] == (64, 1, 1), k
     cfg = loom.launch_config_invoke(i8, [28672, 8192, 8])
     assert cfg["workgroups"][0] == 1792
     # 4 waves split k per 16-row tile; LDS: 3 waves' int32 partial tiles (1 KiB

@@ -300,13 +300,15 @@ I8_CASES = [
     # lanes per row; a wave per 64 rows; groups partly past the row):
     (1, 4, 1), (7, 4, 1), (5, 0, 1), (100, 8, 1), (65, 16, 1), (130, 20, 1), (64, 64, 1), (200, 100, 1),
     (129, 252, 1), (1000, 256, 1), (77, 260, 1), (300, 508, 1), (4097, 512, 1),
-    # rows of 513 bytes to 4 KiB, a wave per block of rows (whole and partly
-    # filled last records, blocks that end mid-matrix):
-    (3, 516, 1), (8, 1024, 1), (9, 1028, 1), (33, 1040, 1), (100, 2112, 1), (3000, 1536, 1), (70, 3072, 1),
-    (41, 4092, 1),
-    # rows of 4 KiB or more, a workgroup per row (waves with no record at
-    # all, a partial last record):
-    (17, 8192, 1), (40, 12804, 1), (13, 4096, 1), (19, 4100, 1), (23, 5124, 1), (6, 16896, 1),
+    # rows of whole 1 KiB records, a wave per block of rows (blocks that end
+    # mid-matrix), or a workgroup per row at k = 8192:
+    (8, 1024, 1), (70, 3072, 1), (13, 4096, 1), (17, 8192, 1), (5, 16384, 1),
+    # other rows longer than 512 bytes in groups of rows per record: 4 rows x
+    # 256 B pieces (partial last pieces when k is not a multiple of 256) or 2
+    # rows x 512 B, groups and waves that end mid-matrix
+    (3, 516, 1), (200, 528, 1), (200, 768, 1), (9, 1028, 1), (33, 1040, 1), (77, 1280, 1), (100, 2112, 1),
+    (3000, 1536, 1), (257, 2560, 1), (41, 4092, 1), (19, 4100, 1), (130, 4608, 1), (23, 5124, 1),
+    (5, 8704, 1), (40, 12804, 1), (6, 16896, 1),
     (3, 64, 2), (15, 256, 3), (16, 260, 8), (17, 1000, 8), (100, 8192, 8), (33, 64, 16), (40, 512, 17),
     (20, 1024, 32), (18, 320, 33), (16, 4096, 64), (1, 4, 2), (31, 8, 5),
     # the tile kernel's k split: 1 wave per tile (k <= 2048, several records),
@@ -341,8 +343,8 @@ def test_i8_dequant_dot(loom, device, rows, k, batch):
 
 
 @pytest.mark.parametrize("rows,k,batch", [(70, 4096, 8), (70, 4096, 16), (70, 4096, 33), (70, 4096, 1),
-                                           (70, 5000, 1), (70, 1536, 1), (70, 1028, 1), (130, 100, 1),
-                                           (130, 12, 1)])
+                                           (70, 8192, 1), (70, 5000, 1), (70, 1536, 1), (70, 1028, 1),
+                                           (130, 100, 1), (130, 12, 1)])
 def test_i8_unaligned_operands(loom, device, rows, k, batch):
     # weights and vectors starting 4 bytes past a 16-byte boundary: the kernels
     # read them as single words instead of 16-byte groups (for one vector in
