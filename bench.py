@@ -302,6 +302,38 @@ def main():
         del x3
         torch.cuda.empty_cache()
         seg3 = (out3.cpu().numpy(), t3.cpu().numpy(), L.cpu().numpy(), off.cpu().numpy())
+
+        # Few long segments (4 x 1,048,576 rows x 256 columns, 4 GiB): every
+        # segment is split into parts summed in row order whose sums are added
+        # in part order (outside the step; parity in the tests).
+        S4 = 4
+        off4 = torch.arange(S4 + 1, dtype=torch.int64, device=dev) * (1 << 20)
+        x34 = synth.segment_matrix(synth.SEGMENTS.seed, S4 << 20, CS, device=dev)
+        out34 = torch.empty(S4, CS, device=dev)
+        bytes34 = (S4 << 20) * CS * 4 + (S4 + 1) * 8 + S4 * CS * 4
+        n34 = max(4, K // 5)
+        reps34 = []
+        for _ in range(REPS):
+            torch.cuda.synchronize()
+            loom.segment_sums(x34, off4, out34)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n34):
+                loom.segment_sums(x34, off4, out34)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps34.append(e0.elapsed_time(e1) / n34)
+        ms34 = sum(reps34) / REPS
+        reps34.sort()
+        parts["segment_sums_4x1M"] = {
+            "bytes": bytes34, "us": round(ms34 * 1e3, 1), "GB/s": round(bytes34 / (ms34 * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(bytes34 / (ms34 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "us_median": round(reps34[REPS // 2] * 1e3, 1), "us_min": round(reps34[0] * 1e3, 1),
+            "parts_per_segment": loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"),
+                                                           [S4, CS, S4 << 20])["workgroups"][0] // S4}
+        log(f"few long segments: {parts['segment_sums_4x1M']}")
+        del x34, out34
+        torch.cuda.empty_cache()
         parts["segment_sums"] = {"bytes": bytes3, "us": round(ms3 * 1e3, 1), "GB/s": round(gbs3, 1),
                                  "frac_of_peak": round(gbs3 / HBM_PEAK_GBS, 4),
                                  "us_median": round(reps3[REPS // 2] * 1e3, 1), "us_min": round(reps3[0] * 1e3, 1),

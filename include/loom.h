@@ -84,7 +84,7 @@ typedef struct loom_launch_config {
  *   "copy_f32"        (n)
  *   "row_sum_tiles"   (count)
  *   "row_sums"        (rows, cols)
- *   "segment_sums"    (segments, cols)
+ *   "segment_sums"    (segments, cols, total_rows)
  *   "i8_dequant_dot"  (rows, k, batch)
  *   "packed_dot"      (outputs, count, streams)
  *   "sum_guarded_rows" (count)
@@ -165,7 +165,17 @@ int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t row_stride
  *     out[s][c] = sum_{offsets[s] <= r < offsets[s+1]} x[r][c]              *
  *     tail_counts[s] = (offsets[s+1] - offsets[s]) mod 8                    *
  * Each column accumulates its rows in row order in f32, so every output is  *
- * the in-order recurrence (an empty segment gives +0.0).                    *
+ * the in-order recurrence bit for bit (an empty segment gives +0.0) --      *
+ * except for a few long segments: when segments x ceil(cols / 256) < 192    *
+ * and the segments average at least 1024 rows (total_rows / segments), each *
+ * segment is split into P contiguous parts of at least 512 rows on average  *
+ * (P * segments * ceil(cols / 256) <= 4096), each part summed in row order, *
+ * and the P part sums added in a fixed order (contiguous runs of           *
+ * ceil(P / 16) parts in part order, then the run sums in run order): the    *
+ * same bits on every call, within 1e-5 * sum|x| of the in-order sum.  The   *
+ * partials (4 * segments * P * cols bytes, at most 4 MiB) are then taken    *
+ * from HIP's stream-ordered allocator on `stream` (hipMallocAsync /         *
+ * hipFreeAsync): the one case where a call allocates device memory.         *
  *   x           : f32[total_rows][cols], device, row-major, 4-byte aligned  *
  *   total_rows  : rows in x, 0 <= total_rows <= 2^40                        *
  *   offsets     : int64[segments+1], device, CSR row offsets.  A segment    *
@@ -176,6 +186,7 @@ int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t row_stride
  *   cols        : 0 <= cols <= 2^20                                         *
  *   out         : f32[segments][cols], device                               *
  *   tail_counts : int32[segments], device, or NULL                          *
+ * LOOM_ERR_DEVICE also when the stream-ordered allocation fails.            *
  * ------------------------------------------------------------------------ */
 int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets,
                       int64_t segments, int64_t cols, float *out,

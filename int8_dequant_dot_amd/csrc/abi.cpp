@@ -95,15 +95,28 @@ extern "C" int loom_segment_sums(const float *x, int64_t total_rows, const int64
         total_rows > kMaxTotalRows)
         return LOOM_ERR_RANGE;
     loom_launch_config cfg;
-    const int64_t w[2] = {segments, cols};
+    const int64_t w[3] = {segments, cols, total_rows};
     if (int st = loom::evaluate_launch(loom::kSegmentSums, w, &cfg)) return st;
     if (segments == 0) return LOOM_OK;
     if (!offsets || (!out && cols > 0) || (!x && total_rows > 0 && cols > 0)) return LOOM_ERR_NULL;
     if (misaligned(offsets, 8) || misaligned(x, 4) || misaligned(out, 4) || misaligned(tail_counts, 4))
         return LOOM_ERR_ALIGN;
+    const int64_t partial_bytes = loom::segment_sums_partial_bytes(segments, cols, total_rows);
+    if (partial_bytes == 0)
+        return launch([&] {
+            return loom::launch_segment_sums(cfg, x, total_rows, offsets, segments, (int)cols, out, tail_counts,
+                                             nullptr, (hipStream_t)stream);
+        });
+    // few long segments: the partials live in stream-ordered memory, taken
+    // and given back on the caller's stream around the two passes
     return launch([&] {
-        return loom::launch_segment_sums(cfg, x, total_rows, offsets, segments, (int)cols, out, tail_counts,
-                                         (hipStream_t)stream);
+        void *partial = nullptr;
+        hipError_t e = hipMallocAsync(&partial, (size_t)partial_bytes, (hipStream_t)stream);
+        if (e != hipSuccess) return e;
+        e = loom::launch_segment_sums(cfg, x, total_rows, offsets, segments, (int)cols, out, tail_counts,
+                                      static_cast<float *>(partial), (hipStream_t)stream);
+        const hipError_t f = hipFreeAsync(partial, (hipStream_t)stream);
+        return e != hipSuccess ? e : f;
     });
 }
 

@@ -82,6 +82,39 @@ constexpr int row_sums_waves_per_row(int64_t cols) {
 // Columns of one segment-sum wave: a segment of a wider matrix is spread over
 // ceil(cols / kSegmentBlockCols) waves (a 1 KiB record per row each).
 constexpr int kSegmentBlockCols = 256;
+// Few long segments.  A launch of fewer than kSegmentSplitMinWaves waves
+// (segments x column blocks) whose segments average at least
+// 2 * kSegmentSplitMinRows rows splits every segment into P contiguous parts
+// of at least kSegmentSplitMinRows rows on average, P * waves at most
+// kSegmentSplitWaves: each part is summed in row order into a partial, and a
+// second pass adds each segment's P partials in a fixed order (contiguous
+// runs of parts in part order, then the runs in run order; one
+// kSegmentCombineWaves-wave workgroup per segment and column block).  The
+// partials need segments * P * cols floats, at most kSegmentSplitWaves * 256
+// (4 MiB).  Returns P, or 1 for the single pass (every column's sum in row
+// order).  Over 4 GiB of 256-column rows (one MI355X), the single pass took
+// 75.4 ms for one segment, 19.0 ms for 4, 1366 us for 64, 704 us for 160 and
+// 606 us for 200 segments; split, 681, 650, 652, 657 and 637 us.
+#ifndef LOOM_SEGMENT_SPLIT_MIN_WAVES
+#define LOOM_SEGMENT_SPLIT_MIN_WAVES 192
+#endif
+constexpr int64_t kSegmentSplitMinWaves = LOOM_SEGMENT_SPLIT_MIN_WAVES;
+constexpr int kSegmentCombineWaves = 16;
+constexpr int64_t kSegmentSplitWaves = 4096;
+constexpr int64_t kSegmentSplitMinRows = 512;
+constexpr int64_t kSegmentSplitMaxBytes = kSegmentSplitWaves * kSegmentBlockCols * 4;
+constexpr int segment_sums_parts(int64_t segments, int64_t cols, int64_t total_rows) {
+    const int64_t blocks = cols > 0 ? (cols + kSegmentBlockCols - 1) / kSegmentBlockCols : 1;
+    if (segments <= 0 || cols <= 0 || segments * blocks >= kSegmentSplitMinWaves) return 1;
+    const int64_t by_waves = kSegmentSplitWaves / (segments * blocks);
+    const int64_t by_rows = total_rows / segments / kSegmentSplitMinRows;
+    const int64_t p = by_waves < by_rows ? by_waves : by_rows;
+    return p >= 2 ? (int)p : 1;
+}
+constexpr int64_t segment_sums_partial_bytes(int64_t segments, int64_t cols, int64_t total_rows) {
+    const int p = segment_sums_parts(segments, cols, total_rows);
+    return p > 1 ? segments * p * cols * 4 : 0;
+}
 
 // Blocking of the int8 kernels.  One vector always runs a v_dot4 GEMV, in
 // one of four forms by row length k (bytes):
@@ -283,9 +316,11 @@ hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *valu
                                 int32_t *tail_count, hipStream_t stream);
 hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int rows, int cols,
                            int64_t row_stride, float *out, hipStream_t stream);
+// partial: segment_sums_partial_bytes of device memory when the launch splits
+// (cfg must be the geometry evaluate_launch gives for the same workload).
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
                                const int64_t *offsets, int64_t segments, int cols, float *out,
-                               int32_t *tail_counts, hipStream_t stream);
+                               int32_t *tail_counts, float *partial, hipStream_t stream);
 hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,
                                  const int32_t *x, const float *x_scale, int rows, int k_words,
                                  int batch, float *out, int32_t *acc, hipStream_t stream);

@@ -67,14 +67,17 @@ int geo_row_sums(const int64_t *w, loom_launch_config *c) {
     return set(c, ceil_div(w[0], int64_t(kTileRows) * kRowSumsTilesPerWave), kSubgroupSize, 0);
 }
 
-// segment_sums(segments, cols): one wave per segment and block of
-// kSegmentBlockCols columns (at least one block, which also writes the
-// segment's tail count when there are no columns); past 2^26 - 1 segments
-// each wave takes every grid.x-th segment.
+// segment_sums(segments, cols, total_rows): one wave per segment -- or, for a
+// few long segments, per part of a segment (segment_sums_parts) -- and block
+// of kSegmentBlockCols columns (at least one block, which also writes the
+// segment's tail count when there are no columns); past 2^26 - 1 units each
+// wave takes every grid.x-th unit.  A split launch is followed by a pass of
+// one wave per segment and block that adds the parts.
 int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
-    if (w[0] < 0 || w[1] < 0) return LOOM_ERR_RANGE;
+    if (w[0] < 0 || w[1] < 0 || w[2] < 0) return LOOM_ERR_RANGE;
     const int64_t blocks = w[1] > 0 ? ceil_div(w[1], kSegmentBlockCols) : 1;
-    return set2(c, grid_stride_groups(w[0], kSubgroupSize), blocks, kSubgroupSize, 0);
+    const int64_t units = w[0] * segment_sums_parts(w[0], w[1], w[2]);
+    return set2(c, grid_stride_groups(units, kSubgroupSize), blocks, kSubgroupSize, 0);
 }
 
 // i8_dequant_dot(rows, k, batch): for one vector, by gemv_form(k), one wave
@@ -145,7 +148,7 @@ const Export kExports[kExportCount] = {
     {"copy_f32", 1, geo_copy},
     {"row_sum_tiles", 1, geo_row_sum_tiles},
     {"row_sums", 2, geo_row_sums},
-    {"segment_sums", 2, geo_segment_sums},
+    {"segment_sums", 3, geo_segment_sums},
     {"i8_dequant_dot", 3, geo_i8},
     {"packed_dot", 3, geo_packed_dot},
     {"sum_guarded_rows", 1, geo_sum_guarded_rows},

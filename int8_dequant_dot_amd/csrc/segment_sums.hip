@@ -13,52 +13,64 @@ template <> struct seg_vec<4> { typedef float4v type; };
 // ----------------------------------------------------------------------------
 // TUNE §Keep one checked source for experiments (@sum_rows): each lane sums
 // its own column over the rows, one load and one add per row, in row order.
-// Here one wave owns one segment and one block of kSegmentBlockCols columns
-// (blockIdx.y picks the block, so a wide matrix spreads a segment over several
-// waves without changing any column's order).  A lane owns VEC adjacent
-// columns of each 64*VEC-column part of the block (one 1 KiB coalesced record
-// per row for VEC = 4) and walks the segment's rows in order -- the full
-// 8-row tiles and then the tail, which are consecutive -- with the next rows
-// read ahead.  No cross-lane reduction is needed, and every column's sum is
-// the same in-order f32 recurrence a serial loop computes.  Lanes past the
-// last column load from the start of the row instead (always inside the
-// matrix) and never store, so every lane issues the same loads and the
-// read-ahead keeps its partial waits.  Segments with bad offsets are reported
-// in-band and read nothing.
+// Here one wave owns one unit -- a segment, or with PARTS a part of one -- and
+// one block of kSegmentBlockCols columns (blockIdx.y picks the block, so a
+// wide matrix spreads a segment over several waves without changing any
+// column's order).  A lane owns VEC adjacent columns of each 64*VEC-column
+// part of the block (one 1 KiB coalesced record per row for VEC = 4) and
+// walks the unit's rows in order -- the full 8-row tiles and then the tail,
+// which are consecutive -- with the next rows read ahead.  No cross-lane
+// reduction is needed, and every column's sum is the same in-order f32
+// recurrence a serial loop computes.  Lanes past the last column load from
+// the start of the row instead (always inside the matrix) and never store, so
+// every lane issues the same loads and the read-ahead keeps its partial waits.
+// Segments with bad offsets are reported in-band and read nothing.
+//
+// PARTS (few long segments, segment_sums_parts): unit u is part u mod P of
+// segment u / P, the rows [len * p / P, len * (p + 1) / P) of the segment,
+// and the wave writes its partial column sums to dst = partial[u][cols];
+// segment_sums_combine_kernel then adds the P partials of each segment in
+// part order.  Without PARTS, unit s is segment s and dst = out[s][cols].
 // ----------------------------------------------------------------------------
-template <int VEC, bool FULL, int DEPTH>
+template <int VEC, bool FULL, int DEPTH, bool PARTS>
 __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__restrict__ x, int64_t total_rows,
-                                                             const int64_t *__restrict__ offsets, int64_t segments,
-                                                             int cols, float *__restrict__ out,
+                                                             const int64_t *__restrict__ offsets, int64_t units,
+                                                             int parts, int cols, float *__restrict__ dst,
                                                              int32_t *__restrict__ tail_counts) {
     typedef typename seg_vec<VEC>::type V;
     constexpr int kBlock = kWave * VEC;
     const int lane = lane_id();
     const int block_first = blockIdx.y * kSegmentBlockCols;
     const int block_end = min(cols, block_first + kSegmentBlockCols);
-    // one segment per wave; past the grid's work-item limit, every grid.x-th segment
-    for (int64_t s = blockIdx.x; s < segments; s += gridDim.x) {
+    // one unit per wave; past the grid's work-item limit, every grid.x-th unit
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const int64_t s = PARTS ? u / parts : u;
+        const int p = PARTS ? (int)(u - s * parts) : 0;
         const int64_t begin = offsets[s];
         const int64_t end = offsets[s + 1];
-        float *o = out + s * cols;
+        float *o = dst + u * cols;
+        const bool writes_tail = p == 0 && blockIdx.y == 0 && tail_counts;
 
         if (!(begin >= 0 && begin <= end && end <= total_rows)) {
             for (int c = block_first + lane; c < block_end; c += kWave) o[c] = __builtin_nanf("");
-            if (lane == 0 && blockIdx.y == 0 && tail_counts) tail_counts[s] = -1;
+            if (lane == 0 && writes_tail) tail_counts[s] = -1;
             continue;
         }
         const int64_t length = end - begin;
-        if (lane == 0 && blockIdx.y == 0 && tail_counts) tail_counts[s] = (int32_t)(length & (kTileRows - 1));
+        if (lane == 0 && writes_tail) tail_counts[s] = (int32_t)(length & (kTileRows - 1));
+        // this unit's rows (the whole segment without PARTS)
+        const int64_t first = PARTS ? begin + length * p / parts : begin;
+        const int64_t count = PARTS ? begin + length * (p + 1) / parts - first : length;
 
         for (int cb = block_first; cb < block_end; cb += kBlock) {
             const int c = cb + lane * VEC;
             const bool active = FULL || c < cols;
             // Row base of the next load (wave-uniform) plus the lane's column.
-            const float *rp = x + begin * cols + cb;
+            const float *rp = x + first * cols + cb;
             const int lane_col = active ? lane * VEC : -cb;  // inactive lanes read the row's first columns
             V acc = V(0.0f);
             pipelined<DEPTH, V>(
-                length,
+                count,
                 [&]() {
                     const V v = load_stream(reinterpret_cast<const V *>(rp + lane_col));
                     rp += cols;
@@ -66,6 +78,51 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
                 },
                 [&](V v) { acc += v; });
             if (active) *reinterpret_cast<V *>(o + c) = acc;
+        }
+    }
+}
+
+// The second pass of a split launch: one workgroup of kSegmentCombineWaves
+// waves per segment and 256-column block, a lane per column.  Wave w adds,
+// in part order, the partials of its contiguous run of parts -- parts
+// w * R .. w * R + R - 1, R = ceil(P / kSegmentCombineWaves) -- with the
+// partials read ahead, and out[s][c] is the sum of the run sums in run order,
+// all in f32 from +0.0: a fixed association of the P part sums, so a call
+// gives the same bits every time.  A segment with bad offsets has NaN
+// partials, so its outputs stay NaN.
+template <int DEPTH>
+__global__ __launch_bounds__(kWave * kSegmentCombineWaves) void segment_sums_combine_kernel(
+    const float *__restrict__ partial, int64_t segments, int parts, int cols, float *__restrict__ out) {
+    __shared__ float run[kSegmentCombineWaves][kWave];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int per = (parts + kSegmentCombineWaves - 1) / kSegmentCombineWaves;
+    const int first = min(parts, wave * per);
+    const int n = min(parts, first + per) - first;
+    const int block_first = blockIdx.y * kSegmentBlockCols;
+    const int block_end = min(cols, block_first + kSegmentBlockCols);
+    for (int64_t s = blockIdx.x; s < segments; s += gridDim.x) {
+        for (int c0 = block_first; c0 < block_end; c0 += kWave) {
+            const int c = c0 + lane;
+            const bool active = c < block_end;
+            const float *pp = partial + (s * parts + first) * cols + (active ? c : block_first);
+            float acc = 0.0f;
+            pipelined<DEPTH, float>(
+                n,
+                [&]() {
+                    const float v = *pp;
+                    pp += cols;
+                    return v;
+                },
+                [&](float v) { acc = acc + v; });
+            run[wave][lane] = acc;
+            __syncthreads();
+            if (wave == 0) {
+                float sum = 0.0f;
+                for (int v = 0; v < kSegmentCombineWaves; ++v) sum = sum + run[v][lane];
+                if (active) out[s * cols + c] = sum;
+            }
+            __syncthreads();  // run[] is rewritten next
         }
     }
 }
@@ -83,53 +140,73 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
 #define LOOM_SEGMENT_SUMS_DEPTH 8
 #endif
 constexpr int kSegmentDepth = LOOM_SEGMENT_SUMS_DEPTH;
+constexpr int kSegmentCombineDepth = 8;
 constexpr int segment_sums_depth(int64_t waves, int cols) {
     const int by_waves = waves <= 256 ? 4 * kSegmentDepth : waves <= 1024 ? 2 * kSegmentDepth : kSegmentDepth;
     const int by_width = cols <= 64 ? 4 * kSegmentDepth : cols <= 128 ? 2 * kSegmentDepth : kSegmentDepth;
     return by_waves > by_width ? by_waves : by_width;
 }
 
-template <int DEPTH>
+template <int DEPTH, bool PARTS>
 static void launch_segment_sums_depth(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
-                                      const int64_t *offsets, int64_t segments, int cols, float *out,
+                                      const int64_t *offsets, int64_t units, int parts, int cols, float *dst,
                                       int32_t *tail_counts, hipStream_t stream) {
     if (vec4) {
         if (cols % (kWave * 4) == 0)
-            segment_sums_kernel<4, true, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, segments, cols, out,
-                                                                            tail_counts);
+            segment_sums_kernel<4, true, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
+                                                                                   parts, cols, dst, tail_counts);
         else
-            segment_sums_kernel<4, false, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, segments, cols, out,
-                                                                             tail_counts);
+            segment_sums_kernel<4, false, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
+                                                                                    parts, cols, dst, tail_counts);
     } else {
         if (cols % kWave == 0)
-            segment_sums_kernel<1, true, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, segments, cols, out,
-                                                                            tail_counts);
+            segment_sums_kernel<1, true, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
+                                                                                   parts, cols, dst, tail_counts);
         else
-            segment_sums_kernel<1, false, DEPTH><<<grid, block, 0, stream>>>(x, total_rows, offsets, segments, cols, out,
-                                                                             tail_counts);
+            segment_sums_kernel<1, false, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
+                                                                                    parts, cols, dst, tail_counts);
+    }
+}
+
+template <bool PARTS>
+static void launch_segment_units(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
+                                 const int64_t *offsets, int64_t units, int parts, int cols, float *dst,
+                                 int32_t *tail_counts, hipStream_t stream) {
+    switch (segment_sums_depth((int64_t)grid.x * grid.y, cols)) {
+        case 4 * kSegmentDepth:
+            launch_segment_sums_depth<4 * kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
+                                                                 parts, cols, dst, tail_counts, stream);
+            break;
+        case 2 * kSegmentDepth:
+            launch_segment_sums_depth<2 * kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
+                                                                 parts, cols, dst, tail_counts, stream);
+            break;
+        default:
+            launch_segment_sums_depth<kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
+                                                             parts, cols, dst, tail_counts, stream);
+            break;
     }
 }
 
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
                                const int64_t *offsets, int64_t segments, int cols, float *out,
-                               int32_t *tail_counts, hipStream_t stream) {
+                               int32_t *tail_counts, float *partial, hipStream_t stream) {
     const dim3 grid(cfg.workgroups[0], cfg.workgroups[1]), block(cfg.workgroup_size[0]);
-    const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0) &&
+    const int parts = segment_sums_parts(segments, cols, total_rows);
+    float *dst = parts > 1 ? partial : out;  // what the row pass writes
+    const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
                       (cols % 4 == 0);
-    switch (segment_sums_depth((int64_t)cfg.workgroups[0] * cfg.workgroups[1], cols)) {
-        case 4 * kSegmentDepth:
-            launch_segment_sums_depth<4 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, segments, cols,
-                                                         out, tail_counts, stream);
-            break;
-        case 2 * kSegmentDepth:
-            launch_segment_sums_depth<2 * kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, segments, cols,
-                                                         out, tail_counts, stream);
-            break;
-        default:
-            launch_segment_sums_depth<kSegmentDepth>(grid, block, vec4, x, total_rows, offsets, segments, cols,
-                                                     out, tail_counts, stream);
-            break;
+    if (parts <= 1) {
+        launch_segment_units<false>(grid, block, vec4, x, total_rows, offsets, segments, 1, cols, out, tail_counts,
+                                    stream);
+        return hipGetLastError();
     }
+    launch_segment_units<true>(grid, block, vec4, x, total_rows, offsets, segments * parts, parts, cols, partial,
+                               tail_counts, stream);
+    if (hipError_t e = hipGetLastError()) return e;
+    const dim3 cgrid((unsigned)grid_stride_groups(segments, kWave * kSegmentCombineWaves), cfg.workgroups[1]);
+    segment_sums_combine_kernel<kSegmentCombineDepth>
+        <<<cgrid, dim3(kWave * kSegmentCombineWaves), 0, stream>>>(partial, segments, parts, cols, out);
     return hipGetLastError();
 }
 

@@ -101,9 +101,19 @@ def test_launch_config_tiles(loom):
     assert loom.launch_config_invoke(rs, [100000, 129])["workgroups"][0] == -(-100000 // 16)  # tiled
     assert loom.launch_config_invoke(rs, [8, 1 << 24])["workgroup_size"][0] == 1024
     seg = loom.launch_config_lookup("segment_sums")
-    assert loom.launch_config_invoke(seg, [16384, 256])["workgroups"] == (16384, 1, 1)
-    assert loom.launch_config_invoke(seg, [100, 1000])["workgroups"] == (100, 4, 1)  # a wave per 256 columns
-    assert loom.launch_config_invoke(seg, [5, 0])["workgroups"] == (5, 1, 1)  # still writes the tail counts
+    assert loom.launch_config_invoke(seg, [16384, 256, 33640572])["workgroups"] == (16384, 1, 1)
+    assert loom.launch_config_invoke(seg, [100, 1000, 5000])["workgroups"] == (100, 4, 1)  # a wave per 256 columns
+    assert loom.launch_config_invoke(seg, [5, 0, 10**9])["workgroups"] == (5, 1, 1)  # still writes the tail counts
+    # few long segments (fewer than 192 segment waves, at least 1024 rows on
+    # average): P parts per segment, parts of at least 512 rows on average,
+    # P * waves <= 4096
+    for segments, cols, total, parts in ((4, 256, 4 * 2**20, 1024), (3, 256, 120000, 78), (3, 1000, 120000, 78),
+                                         (47, 1000, 10**7, 21), (48, 1000, 10**7, 1), (191, 256, 10**8, 21),
+                                         (192, 256, 10**8, 1), (10, 256, 10239, 1), (10, 256, 10240, 2),
+                                         (2, 2**20, 10**6, 1), (1, 4096, 2**20, 256)):
+        blocks = -(-cols // 256)
+        cfg = loom.launch_config_invoke(seg, [segments, cols, total])
+        assert cfg["workgroups"] == (segments * parts, blocks, 1), (segments, cols, total)
     i8 = loom.launch_config_lookup("i8_dequant_dot")
     # one vector, always a v_dot4 GEMV: rows of 6 to 8 whole 1 KiB records a
     # workgroup per row with a wave per 2 records (LDS: the wave totals) ...
@@ -209,9 +219,9 @@ def test_launch_config_errors(loom, lib):
     # past the limit (segments, long rows, tokens, long GEMV rows)
     cap64, cap256 = (2 ** 32 - 1) // 64, (2 ** 32 - 1) // 256
     seg = loom.launch_config_lookup("segment_sums")
-    assert loom.launch_config_invoke(seg, [cap64, 256])["workgroups"] == (cap64, 1, 1)
-    assert loom.launch_config_invoke(seg, [cap64 + 1, 256])["workgroups"] == (cap64, 1, 1)
-    assert loom.launch_config_invoke(seg, [2 ** 31 - 2, 1000])["workgroups"] == (cap64, 4, 1)
+    assert loom.launch_config_invoke(seg, [cap64, 256, 0])["workgroups"] == (cap64, 1, 1)
+    assert loom.launch_config_invoke(seg, [cap64 + 1, 256, 0])["workgroups"] == (cap64, 1, 1)
+    assert loom.launch_config_invoke(seg, [2 ** 31 - 2, 1000, 2**40])["workgroups"] == (cap64, 4, 1)
     rs = loom.launch_config_lookup("row_sums")
     assert loom.launch_config_invoke(rs, [2 ** 24, 4096])["workgroups"] == (cap256, 1, 1)
     assert loom.launch_config_invoke(rs, [2 ** 31 - 1, 1 << 24])["workgroups"] == ((2 ** 32 - 1) // 1024, 1, 1)

@@ -164,7 +164,7 @@ def test_segment_sums_past_grid_limit(loom, device):
     off = synth.segment_offsets(L)
     total = int(off[-1])
     x = synth.segment_matrix(synth.SEGMENTS.seed, total, cols, device=device)
-    cfg = loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"), [S, cols])
+    cfg = loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"), [S, cols, total])
     assert cfg["workgroups"][0] < S
     out, tails = loom.segment_sums(x, off.to(device))
     g, t = _np(out), _np(tails)

@@ -242,6 +242,72 @@ def test_segment_sums_bad_offsets_reported(loom, device):
     assert np.all(np.isnan(g[3]))  # [12, 12) lies beyond the 10 rows
 
 
+# Few long segments: fewer than 1024 segment waves and at least 1024 rows per
+# segment on average split every segment into P parts, each summed in row
+# order, and add the part sums in part order (a fixed order: the same bits
+# on every call, within the f32 tolerance of the in-order sums).
+SPLIT_CASES = [
+    ([100000], 256),                      # one segment, 195 parts
+    ([40000, 0, 35000], 256),             # an empty segment among long ones
+    ([3000, 50000, 7, 20000], 1000),      # four column blocks, a 7-row segment with mostly empty parts
+    ([60000, 12345], 257),                # 32-bit path (cols % 4 != 0), two blocks
+    ([30000, 30000], 100),                # one partial block
+]
+
+
+def _parts(loom, segments, cols, total):
+    cfg = loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"), [segments, cols, total])
+    return cfg["workgroups"][0] // segments
+
+
+@pytest.mark.parametrize("lengths,cols", SPLIT_CASES)
+def test_segment_sums_split_within_tolerance(loom, device, lengths, cols):
+    L = torch.tensor(lengths, dtype=torch.int64)
+    off = synth.segment_offsets(L)
+    total = int(off[-1])
+    assert _parts(loom, len(lengths), cols, total) > 1
+    x = synth.segment_rows(synth.SEGMENTS.seed, 0, total, cols)
+    dx, doff = x.to(device), off.to(device)
+    out, tails = loom.segment_sums(dx, doff)
+    g = _np(out)
+    ref, rtails, d, a = oracle.segment_sums(x.numpy(), off.numpy())
+    assert_sum_close(g, ref, d, a, what=f"split {lengths}x{cols}")
+    assert np.array_equal(_np(tails), rtails)
+    assert np.array_equal(g[L.numpy() == 0].view(np.uint32), ref[L.numpy() == 0].view(np.uint32))  # +0.0
+    again, _ = loom.segment_sums(dx, doff)
+    assert np.array_equal(_np(again).view(np.uint32), g.view(np.uint32))  # the same bits on every call
+
+
+def test_segment_sums_split_integer_exact(loom, device):
+    # small integers: every partial and every sum is exact in f32, so the split
+    # sums equal the in-order recurrence bit for bit
+    lengths, cols = [70000, 3, 41000], 256
+    L = torch.tensor(lengths, dtype=torch.int64)
+    off = synth.segment_offsets(L)
+    total = int(off[-1])
+    assert _parts(loom, 3, cols, total) > 1
+    x = (synth.randint(93, 1, 0, total * cols, -8, 8).view(total, cols)).to(torch.float32)
+    out, tails = loom.segment_sums(x.to(device), off.to(device))
+    ref, rtails, _, _ = oracle.segment_sums(x.numpy(), off.numpy())
+    assert np.array_equal(_np(out).view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(_np(tails), rtails)
+
+
+def test_segment_sums_split_bad_offsets(loom, device):
+    total, cols = 90000, 256
+    x = synth.segment_rows(synth.SEGMENTS.seed, 0, total, cols)
+    off = torch.tensor([0, 40000, 30000, 90000, 90001], dtype=torch.int64)  # decreasing, then past the rows
+    assert _parts(loom, 4, cols, total) > 1
+    out, tails = loom.segment_sums(x.to(device), off.to(device))
+    g, t = _np(out), _np(tails)
+    ref, _, d, a = oracle.segment_sums(x.numpy()[:40000], np.array([0, 40000]))
+    assert_sum_close(g[0], ref[0], d[0], a[0], what="split segment before bad ones")
+    assert np.all(np.isnan(g[1])) and np.all(np.isnan(g[3]))
+    ref2, _, d2, a2 = oracle.segment_sums(x.numpy()[30000:90000], np.array([0, 60000]))
+    assert_sum_close(g[2], ref2[0], d2[0], a2[0], what="split segment after a bad one")
+    assert list(t) == [0, -1, 0, -1]
+
+
 def test_segment_sums_full_size(loom, device):
     S, cols = 16384, 256
     L = synth.segment_lengths(synth.SEGMENTS.seed, S, 4096)
