@@ -193,6 +193,24 @@ int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets
                       int32_t *tail_counts, void *stream);
 
 /* ------------------------------------------------------------------------ *
+ * For callers that cannot allocate device memory -- code under HIP graph    *
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same   *
+ * operation, arguments, checks and results (the same bits) as              *
+ * loom_segment_sums, but a split launch keeps its partials in the library's *
+ * own static device array of 4 MiB (one per GPU the library runs on, kept   *
+ * until the process ends) instead of stream-ordered memory, so no call      *
+ * allocates.  Every call on a GPU shares that GPU's array and it keeps the  *
+ * last call's contents (each split launch writes every partial it reads):   *
+ * calls that may overlap on one GPU -- on different streams or threads --   *
+ * race and must be ordered by the caller.  LOOM_ERR_RANGE if a split would  *
+ * need more than the array holds (the split rule keeps every launch within  *
+ * it).                                                                      *
+ * ------------------------------------------------------------------------ */
+int loom_segment_sums_noalloc(const float *x, int64_t total_rows, const int64_t *offsets,
+                              int64_t segments, int64_t cols, float *out,
+                              int32_t *tail_counts, void *stream);
+
+/* ------------------------------------------------------------------------ *
  * Packed signed-byte dequantization with dot accumulation (TUNE §Apply the  *
  * same controls to a packed dot product; scales factored out of the sum).   *
  *     acc[r][b] = sum_{i < k} w[r][i] * x[b][i]          (exact, int32)     *

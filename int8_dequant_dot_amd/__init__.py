@@ -36,12 +36,14 @@ _lib.loom_copy_f32.argtypes = [_p, _p, _i64, _p]
 _lib.loom_row_sum_tiles.argtypes = [_p, _i64, _i64, _p, _p, _p, _p, _p]
 _lib.loom_row_sums.argtypes = [_p, _i64, _i64, _i64, _p, _p]
 _lib.loom_segment_sums.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p, _p]
+_lib.loom_segment_sums_noalloc.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p, _p]
 _lib.loom_i8_dequant_dot.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p]
 _lib.loom_packed_dot.argtypes = [_p, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _p]
 _lib.loom_sum_guarded_rows.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _p]
 _lib.loom_routed_combine.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]
 for _name in ("loom_launch_config_lookup", "loom_launch_config_invoke", "loom_copy_f32", "loom_row_sum_tiles",
-              "loom_row_sums", "loom_segment_sums", "loom_i8_dequant_dot", "loom_packed_dot",
+              "loom_row_sums", "loom_segment_sums", "loom_segment_sums_noalloc", "loom_i8_dequant_dot",
+              "loom_packed_dot",
               "loom_sum_guarded_rows", "loom_routed_combine"):
     getattr(_lib, _name).restype = ctypes.c_int
 
@@ -189,8 +191,11 @@ def row_sums(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
 
 
 def segment_sums(x: torch.Tensor, offsets: torch.Tensor, out: torch.Tensor | None = None,
-                 tail_counts: torch.Tensor | None = None, want_tails: bool = True):
-    """x [total_rows][cols] f32, offsets int64 [S+1] (CSR) -> (out [S][cols], tail_counts int32 [S])."""
+                 tail_counts: torch.Tensor | None = None, want_tails: bool = True, noalloc: bool = False):
+    """x [total_rows][cols] f32, offsets int64 [S+1] (CSR) -> (out [S][cols], tail_counts int32 [S]).
+
+    noalloc=True calls loom_segment_sums_noalloc (no device allocation inside
+    the call; calls that overlap on one GPU must be ordered by the caller)."""
     device, stream = _target(x, "x")
     _dev(x, torch.float32, "x", device)
     _dev(offsets, torch.int64, "offsets", device)
@@ -205,8 +210,9 @@ def segment_sums(x: torch.Tensor, offsets: torch.Tensor, out: torch.Tensor | Non
     if tail_counts is None and want_tails:
         tail_counts = torch.empty(S, dtype=torch.int32, device=x.device)
     _buffer(tail_counts, torch.int32, S, "tail_counts", device, optional=True)
-    _check(_lib.loom_segment_sums(_ptr(x), x.shape[0], _ptr(offsets), S, cols, _ptr(out), _ptr(tail_counts),
-                                  stream), "segment_sums")
+    fn = _lib.loom_segment_sums_noalloc if noalloc else _lib.loom_segment_sums
+    _check(fn(_ptr(x), x.shape[0], _ptr(offsets), S, cols, _ptr(out), _ptr(tail_counts), stream),
+           "segment_sums_noalloc" if noalloc else "segment_sums")
     return out, tail_counts
 
 

@@ -89,18 +89,35 @@ extern "C" int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t
         [&] { return loom::launch_row_sums(cfg, x, (int)rows, (int)cols, row_stride, out, (hipStream_t)stream); });
 }
 
-extern "C" int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets, int64_t segments,
-                                 int64_t cols, float *out, int32_t *tail_counts, void *stream) {
+namespace {
+
+// The checks of both segment-sum entry points, in the documented order; on
+// LOOM_OK with *nothing false, cfg holds the launch geometry.
+int segment_sums_checks(const float *x, int64_t total_rows, const int64_t *offsets, int64_t segments, int64_t cols,
+                        const float *out, const int32_t *tail_counts, loom_launch_config *cfg, bool *nothing) {
+    *nothing = true;
     if (segments < 0 || segments > kMaxRows - 1 || cols < 0 || cols > kMaxSegmentCols || total_rows < 0 ||
         total_rows > kMaxTotalRows)
         return LOOM_ERR_RANGE;
-    loom_launch_config cfg;
     const int64_t w[3] = {segments, cols, total_rows};
-    if (int st = loom::evaluate_launch(loom::kSegmentSums, w, &cfg)) return st;
+    if (int st = loom::evaluate_launch(loom::kSegmentSums, w, cfg)) return st;
     if (segments == 0) return LOOM_OK;
     if (!offsets || (!out && cols > 0) || (!x && total_rows > 0 && cols > 0)) return LOOM_ERR_NULL;
     if (misaligned(offsets, 8) || misaligned(x, 4) || misaligned(out, 4) || misaligned(tail_counts, 4))
         return LOOM_ERR_ALIGN;
+    *nothing = false;
+    return LOOM_OK;
+}
+
+}  // namespace
+
+extern "C" int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets, int64_t segments,
+                                 int64_t cols, float *out, int32_t *tail_counts, void *stream) {
+    loom_launch_config cfg;
+    bool nothing;
+    if (int st = segment_sums_checks(x, total_rows, offsets, segments, cols, out, tail_counts, &cfg, &nothing))
+        return st;
+    if (nothing) return LOOM_OK;
     const int64_t partial_bytes = loom::segment_sums_partial_bytes(segments, cols, total_rows);
     if (partial_bytes == 0)
         return launch([&] {
@@ -117,6 +134,27 @@ extern "C" int loom_segment_sums(const float *x, int64_t total_rows, const int64
                                       static_cast<float *>(partial), (hipStream_t)stream);
         const hipError_t f = hipFreeAsync(partial, (hipStream_t)stream);
         return e != hipSuccess ? e : f;
+    });
+}
+
+extern "C" int loom_segment_sums_noalloc(const float *x, int64_t total_rows, const int64_t *offsets,
+                                         int64_t segments, int64_t cols, float *out, int32_t *tail_counts,
+                                         void *stream) {
+    loom_launch_config cfg;
+    bool nothing;
+    if (int st = segment_sums_checks(x, total_rows, offsets, segments, cols, out, tail_counts, &cfg, &nothing))
+        return st;
+    if (nothing) return LOOM_OK;
+    const int64_t partial_bytes = loom::segment_sums_partial_bytes(segments, cols, total_rows);
+    if (partial_bytes > loom::kSegmentSplitMaxBytes) return LOOM_ERR_RANGE;  // beyond the static array
+    return launch([&] {
+        float *partial = nullptr;
+        if (partial_bytes > 0) {
+            const hipError_t e = loom::segment_scratch(&partial);
+            if (e != hipSuccess) return e;
+        }
+        return loom::launch_segment_sums(cfg, x, total_rows, offsets, segments, (int)cols, out, tail_counts,
+                                         partial, (hipStream_t)stream);
     });
 }
 

@@ -316,6 +316,9 @@ hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *valu
                                 int32_t *tail_count, hipStream_t stream);
 hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int rows, int cols,
                            int64_t row_stride, float *out, hipStream_t stream);
+// The current device's address of the library's static partial array
+// (kSegmentSplitMaxBytes), looked up on the first call on each device.
+hipError_t segment_scratch(float **ptr);
 // partial: segment_sums_partial_bytes of device memory when the launch splits
 // (cfg must be the geometry evaluate_launch gives for the same workload).
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,

@@ -1,10 +1,42 @@
 // segment_sums.hip -- per-segment column sums on gfx950.
 //
 // TUNE = "Tune loop unrolling and pipelining" (Loom pages).
+#include <mutex>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
+// The split pass's partials for callers that cannot allocate
+// (loom_segment_sums_noalloc): a file-scope device array, one per GPU the
+// library runs on, kept until the process ends.  Host code never passes its
+// name to a kernel -- in host code the name is only a stand-in, not a device
+// address -- but the address hipGetSymbolAddress gives for the current device
+// (segment_scratch).
+static __device__ __align__(256) float scratch[loom::kSegmentSplitMaxBytes / sizeof(float)];
+
 namespace loom {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_lock;
+float *scratch_address[kMaxDevices];  // per device, looked up on the first call there
+}  // namespace
+
+hipError_t segment_scratch(float **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(scratch_lock);
+    if (!scratch_address[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_address[dev] = static_cast<float *>(p);
+    }
+    *ptr = scratch_address[dev];
+    return hipSuccess;
+}
 
 template <int VEC> struct seg_vec;
 template <> struct seg_vec<1> { typedef float type; };

@@ -103,13 +103,16 @@ def test_i8_dequant_dot_contract(lib, w, ws, x, xs, out, acc, rows, k, batch):
 
 
 @SETTINGS
-@given(x=PTRS, off=PTRS, out=PTRS, tails=PTRS, total=sizes(2**40), segments=sizes(I31 - 1), cols=sizes(2**20))
-def test_segment_sums_contract(lib, x, off, out, tails, total, segments, cols):
+@given(x=PTRS, off=PTRS, out=PTRS, tails=PTRS, total=sizes(2**40), segments=sizes(I31 - 1), cols=sizes(2**20),
+       noalloc=st.booleans())
+def test_segment_sums_contract(lib, x, off, out, tails, total, segments, cols, noalloc):
+    # loom_segment_sums_noalloc has the same contract
     expect = _status([(RANGE, not (0 <= total <= 2**40 and 0 <= segments < I31 and 0 <= cols <= 2**20))],
                      segments == 0,
                      off is None or (out is None and cols > 0) or (x is None and total > 0 and cols > 0),
                      _mis(off, 8) or _mis(x, 4) or _mis(out, 4) or _mis(tails, 4))
-    assert lib.loom_segment_sums(_p(x), total, _p(off), segments, cols, _p(out), _p(tails), None) == expect
+    fn = lib.loom_segment_sums_noalloc if noalloc else lib.loom_segment_sums
+    assert fn(_p(x), total, _p(off), segments, cols, _p(out), _p(tails), None) == expect
 
 
 @SETTINGS
