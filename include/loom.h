@@ -175,7 +175,12 @@ int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t row_stride
  * same bits on every call, within 1e-5 * sum|x| of the in-order sum.  The   *
  * partials (4 * segments * P * cols bytes, at most 4 MiB) are then taken    *
  * from HIP's stream-ordered allocator on `stream` (hipMallocAsync /         *
- * hipFreeAsync): the one case where a call allocates device memory.         *
+ * hipFreeAsync).  A launch that is not split, of 2 to 2^15 segments         *
+ * averaging at least 512 rows and of at least 2^26 floats, first sorts the  *
+ * segments by length (a one-workgroup pass) so its waves take them longest  *
+ * first; the order index (4 * segments bytes) is taken the same way.  These *
+ * are the only cases where a call allocates device memory; neither changes  *
+ * a bit of output.                                                          *
  *   x           : f32[total_rows][cols], device, row-major, 4-byte aligned  *
  *   total_rows  : rows in x, 0 <= total_rows <= 2^40                        *
  *   offsets     : int64[segments+1], device, CSR row offsets.  A segment    *
@@ -196,11 +201,12 @@ int loom_segment_sums(const float *x, int64_t total_rows, const int64_t *offsets
  * For callers that cannot allocate device memory -- code under HIP graph    *
  * capture, tight serving loops, harnesses that forbid hipMalloc: the same   *
  * operation, arguments, checks and results (the same bits) as              *
- * loom_segment_sums, but a split launch keeps its partials in the library's *
- * own static device array of 4 MiB (one per GPU the library runs on, kept   *
- * until the process ends) instead of stream-ordered memory, so no call      *
- * allocates.  Every call on a GPU shares that GPU's array and it keeps the  *
- * last call's contents (each split launch writes every partial it reads):   *
+ * loom_segment_sums, but a split launch's partials and a longest-first     *
+ * launch's order index live in the library's own static device array of    *
+ * 4 MiB (one per GPU the library runs on, kept until the process ends)      *
+ * instead of stream-ordered memory, so no call allocates.  Every call on a  *
+ * GPU shares that GPU's array and it keeps the last call's contents (each   *
+ * launch writes every word of it that it reads):                            *
  * calls that may overlap on one GPU -- on different streams or threads --   *
  * race and must be ordered by the caller.  LOOM_ERR_RANGE if a split would  *
  * need more than the array holds (the split rule keeps every launch within  *

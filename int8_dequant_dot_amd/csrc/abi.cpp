@@ -118,21 +118,21 @@ extern "C" int loom_segment_sums(const float *x, int64_t total_rows, const int64
     if (int st = segment_sums_checks(x, total_rows, offsets, segments, cols, out, tail_counts, &cfg, &nothing))
         return st;
     if (nothing) return LOOM_OK;
-    const int64_t partial_bytes = loom::segment_sums_partial_bytes(segments, cols, total_rows);
-    if (partial_bytes == 0)
+    const int64_t workspace_bytes = loom::segment_sums_workspace_bytes(segments, cols, total_rows);
+    if (workspace_bytes == 0)
         return launch([&] {
             return loom::launch_segment_sums(cfg, x, total_rows, offsets, segments, (int)cols, out, tail_counts,
                                              nullptr, (hipStream_t)stream);
         });
-    // few long segments: the partials live in stream-ordered memory, taken
-    // and given back on the caller's stream around the two passes
+    // a split launch's partials or a longest-first launch's order index live
+    // in stream-ordered memory, taken and given back on the caller's stream
     return launch([&] {
-        void *partial = nullptr;
-        hipError_t e = hipMallocAsync(&partial, (size_t)partial_bytes, (hipStream_t)stream);
+        void *workspace = nullptr;
+        hipError_t e = hipMallocAsync(&workspace, (size_t)workspace_bytes, (hipStream_t)stream);
         if (e != hipSuccess) return e;
-        e = loom::launch_segment_sums(cfg, x, total_rows, offsets, segments, (int)cols, out, tail_counts,
-                                      static_cast<float *>(partial), (hipStream_t)stream);
-        const hipError_t f = hipFreeAsync(partial, (hipStream_t)stream);
+        e = loom::launch_segment_sums(cfg, x, total_rows, offsets, segments, (int)cols, out, tail_counts, workspace,
+                                      (hipStream_t)stream);
+        const hipError_t f = hipFreeAsync(workspace, (hipStream_t)stream);
         return e != hipSuccess ? e : f;
     });
 }
@@ -145,16 +145,16 @@ extern "C" int loom_segment_sums_noalloc(const float *x, int64_t total_rows, con
     if (int st = segment_sums_checks(x, total_rows, offsets, segments, cols, out, tail_counts, &cfg, &nothing))
         return st;
     if (nothing) return LOOM_OK;
-    const int64_t partial_bytes = loom::segment_sums_partial_bytes(segments, cols, total_rows);
-    if (partial_bytes > loom::kSegmentSplitMaxBytes) return LOOM_ERR_RANGE;  // beyond the static array
+    const int64_t workspace_bytes = loom::segment_sums_workspace_bytes(segments, cols, total_rows);
+    if (workspace_bytes > loom::kSegmentSplitMaxBytes) return LOOM_ERR_RANGE;  // beyond the static array
     return launch([&] {
-        float *partial = nullptr;
-        if (partial_bytes > 0) {
-            const hipError_t e = loom::segment_scratch(&partial);
+        void *workspace = nullptr;
+        if (workspace_bytes > 0) {
+            const hipError_t e = loom::segment_scratch(&workspace);
             if (e != hipSuccess) return e;
         }
         return loom::launch_segment_sums(cfg, x, total_rows, offsets, segments, (int)cols, out, tail_counts,
-                                         partial, (hipStream_t)stream);
+                                         workspace, (hipStream_t)stream);
     });
 }
 

@@ -111,9 +111,37 @@ constexpr int segment_sums_parts(int64_t segments, int64_t cols, int64_t total_r
     const int64_t p = by_waves < by_rows ? by_waves : by_rows;
     return p >= 2 ? (int)p : 1;
 }
-constexpr int64_t segment_sums_partial_bytes(int64_t segments, int64_t cols, int64_t total_rows) {
+// Many long segments of uneven length: a single pass over at least
+// kSegmentOrderMinFloats floats of 2 to kSegmentOrderMaxSegments segments
+// averaging at least kSegmentOrderMinRows rows first sorts the segments by
+// length into coarse buckets (one workgroup, a counting sort, 5-11 us) and
+// its waves take them longest first, so the launch ends on short segments
+// instead of a few long ones running nearly alone.  Every column's sum is
+// still the in-order recurrence: only which wave takes which segment
+// changes.  Back to back, index order -> longest first, segments of
+// U{0..max} rows: 16384 x max 4096 x 256 columns 5085 -> 5008 us, 4096 x 4096
+// x 256 1390 -> 1311 us, 2048 x 4096 x 256 752 -> 674 us, 1000 x 20000 x 64
+// 820 -> 637 us, 4096 x 2048 x 16 182 -> 171 us; with short segments the
+// order pass costs more than it saves (16384 x 512 x 256 693 -> 707 us,
+// 3000 x 200 x 256 56 -> 64 us).  Past kSegmentOrderMaxSegments every wave
+// takes many segments and index order balances well enough.
+constexpr int64_t kSegmentOrderMaxSegments = int64_t(1) << 15;
+constexpr int64_t kSegmentOrderMinRows = 512;
+#ifndef LOOM_SEGMENT_ORDER_MIN_FLOATS
+#define LOOM_SEGMENT_ORDER_MIN_FLOATS (int64_t(1) << 26)
+#endif
+constexpr int64_t kSegmentOrderMinFloats = LOOM_SEGMENT_ORDER_MIN_FLOATS;
+constexpr bool segment_sums_ordered(int64_t segments, int64_t cols, int64_t total_rows) {
+    return segment_sums_parts(segments, cols, total_rows) == 1 && segments >= 2 &&
+           segments <= kSegmentOrderMaxSegments && cols > 0 && total_rows / segments >= kSegmentOrderMinRows &&
+           total_rows * cols >= kSegmentOrderMinFloats;
+}
+// Device memory a launch needs beyond its inputs and outputs: the partials of
+// a split launch, or the order index of a longest-first one (at most
+// kSegmentSplitMaxBytes either way).
+constexpr int64_t segment_sums_workspace_bytes(int64_t segments, int64_t cols, int64_t total_rows) {
     const int p = segment_sums_parts(segments, cols, total_rows);
-    return p > 1 ? segments * p * cols * 4 : 0;
+    return p > 1 ? segments * p * cols * 4 : segment_sums_ordered(segments, cols, total_rows) ? segments * 4 : 0;
 }
 
 // Blocking of the int8 kernels.  One vector always runs a v_dot4 GEMV, in
@@ -316,14 +344,14 @@ hipError_t launch_row_sum_tiles(const loom_launch_config &cfg, const float *valu
                                 int32_t *tail_count, hipStream_t stream);
 hipError_t launch_row_sums(const loom_launch_config &cfg, const float *x, int rows, int cols,
                            int64_t row_stride, float *out, hipStream_t stream);
-// The current device's address of the library's static partial array
+// The current device's address of the library's static workspace array
 // (kSegmentSplitMaxBytes), looked up on the first call on each device.
-hipError_t segment_scratch(float **ptr);
-// partial: segment_sums_partial_bytes of device memory when the launch splits
-// (cfg must be the geometry evaluate_launch gives for the same workload).
+hipError_t segment_scratch(void **ptr);
+// workspace: segment_sums_workspace_bytes of device memory (NULL when that is
+// 0); cfg must be the geometry evaluate_launch gives for the same workload.
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
                                const int64_t *offsets, int64_t segments, int cols, float *out,
-                               int32_t *tail_counts, float *partial, hipStream_t stream);
+                               int32_t *tail_counts, void *workspace, hipStream_t stream);
 hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,
                                  const int32_t *x, const float *x_scale, int rows, int k_words,
                                  int batch, float *out, int32_t *acc, hipStream_t stream);

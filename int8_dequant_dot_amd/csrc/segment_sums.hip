@@ -6,9 +6,10 @@
 #include "device_common.hpp"
 #include "internal.hpp"
 
-// The split pass's partials for callers that cannot allocate
-// (loom_segment_sums_noalloc): a file-scope device array, one per GPU the
-// library runs on, kept until the process ends.  Host code never passes its
+// The workspace (a split launch's partials, a longest-first launch's order
+// index) for callers that cannot allocate (loom_segment_sums_noalloc): a
+// file-scope device array, one per GPU the library runs on, kept until the
+// process ends.  Host code never passes its
 // name to a kernel -- in host code the name is only a stand-in, not a device
 // address -- but the address hipGetSymbolAddress gives for the current device
 // (segment_scratch).
@@ -19,10 +20,10 @@ namespace loom {
 namespace {
 constexpr int kMaxDevices = 64;
 std::mutex scratch_lock;
-float *scratch_address[kMaxDevices];  // per device, looked up on the first call there
+void *scratch_address[kMaxDevices];  // per device, looked up on the first call there
 }  // namespace
 
-hipError_t segment_scratch(float **ptr) {
+hipError_t segment_scratch(void **ptr) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -32,7 +33,7 @@ hipError_t segment_scratch(float **ptr) {
         void *p = nullptr;
         e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
         if (e != hipSuccess) return e;
-        scratch_address[dev] = static_cast<float *>(p);
+        scratch_address[dev] = p;
     }
     *ptr = scratch_address[dev];
     return hipSuccess;
@@ -61,14 +62,16 @@ template <> struct seg_vec<4> { typedef float4v type; };
 // PARTS (few long segments, segment_sums_parts): unit u is part u mod P of
 // segment u / P, the rows [len * p / P, len * (p + 1) / P) of the segment,
 // and the wave writes its partial column sums to dst = partial[u][cols];
-// segment_sums_combine_kernel then adds the P partials of each segment in
-// part order.  Without PARTS, unit s is segment s and dst = out[s][cols].
+// segment_sums_combine_kernel then adds the P partials of each segment.
+// Otherwise unit u is segment order[u] (longest first, segment_sums_ordered)
+// or segment u, and dst = out[s][cols].
 // ----------------------------------------------------------------------------
 template <int VEC, bool FULL, int DEPTH, bool PARTS>
 __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__restrict__ x, int64_t total_rows,
                                                              const int64_t *__restrict__ offsets, int64_t units,
                                                              int parts, int cols, float *__restrict__ dst,
-                                                             int32_t *__restrict__ tail_counts) {
+                                                             int32_t *__restrict__ tail_counts,
+                                                             const int32_t *__restrict__ order) {
     typedef typename seg_vec<VEC>::type V;
     constexpr int kBlock = kWave * VEC;
     const int lane = lane_id();
@@ -76,11 +79,11 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
     const int block_end = min(cols, block_first + kSegmentBlockCols);
     // one unit per wave; past the grid's work-item limit, every grid.x-th unit
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-        const int64_t s = PARTS ? u / parts : u;
+        const int64_t s = PARTS ? u / parts : order ? (int64_t)order[u] : u;
         const int p = PARTS ? (int)(u - s * parts) : 0;
         const int64_t begin = offsets[s];
         const int64_t end = offsets[s + 1];
-        float *o = dst + u * cols;
+        float *o = dst + (PARTS ? u : s) * cols;
         const bool writes_tail = p == 0 && blockIdx.y == 0 && tail_counts;
 
         if (!(begin >= 0 && begin <= end && end <= total_rows)) {
@@ -112,6 +115,84 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
             if (active) *reinterpret_cast<V *>(o + c) = acc;
         }
     }
+}
+
+// The order pass of a longest-first launch (one workgroup): a counting sort
+// of the segments by length bucket -- 0 for an empty segment or bad offsets,
+// else 1 + 4 floor(log2 len) + the two bits below the leading one -- into
+// order[], longest bucket first; within a bucket the order is whatever the
+// atomics give, which changes no output.  Each thread reads the offsets of
+// kOrderBatch segments before it uses any, and keeps their buckets in LDS for
+// the scatter.
+constexpr int kOrderBuckets = 1 + 4 * 42;  // lengths of 2^42 rows and more share the top one
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBatch = 8;
+constexpr int kOrderPerLane = (kOrderBuckets + kWave - 1) / kWave;
+static_assert(kSegmentOrderMaxSegments % (kOrderThreads * kOrderBatch) == 0, "whole batches in the LDS array");
+
+__device__ __forceinline__ int length_bucket(int64_t begin, int64_t end, int64_t total_rows) {
+    if (!(begin >= 0 && begin < end && end <= total_rows)) return 0;
+    const uint64_t len = (uint64_t)(end - begin);
+    const int e = min(63 - __builtin_clzll(len), 41);  // floor(log2 len), capped
+    const int m = e >= 2 ? (int)((len >> (e - 2)) & 3) : (int)((len << (2 - e)) & 3);
+    return 1 + 4 * e + m;
+}
+
+__global__ __launch_bounds__(kOrderThreads) void segment_order_kernel(const int64_t *__restrict__ offsets,
+                                                                      int64_t segments, int64_t total_rows,
+                                                                      int32_t *__restrict__ order) {
+    __shared__ unsigned next[kOrderBuckets];
+    __shared__ uint8_t bucket[kSegmentOrderMaxSegments];
+    const int n = (int)min(segments, kSegmentOrderMaxSegments);
+    for (int b = threadIdx.x; b < kOrderBuckets; b += kOrderThreads) next[b] = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += kOrderThreads * kOrderBatch) {
+        int64_t begin[kOrderBatch], end[kOrderBatch];
+#pragma unroll
+        for (int j = 0; j < kOrderBatch; ++j) {
+            const int s = base + j * kOrderThreads + (int)threadIdx.x;
+            begin[j] = s < n ? offsets[s] : 0;
+            end[j] = s < n ? offsets[s + 1] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kOrderBatch; ++j) {
+            const int s = base + j * kOrderThreads + (int)threadIdx.x;
+            if (s < n) {
+                const int k = length_bucket(begin[j], end[j], total_rows);
+                bucket[s] = (uint8_t)k;
+                atomicAdd(&next[k], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        // first position of each bucket, longest bucket first: lane l holds
+        // the kOrderPerLane buckets kOrderBuckets - 1 - (kOrderPerLane l + j),
+        // and a wave-wide exclusive scan of the lanes' totals places them
+        const int lane = (int)threadIdx.x;
+        unsigned c[kOrderPerLane], own = 0;
+#pragma unroll
+        for (int j = 0; j < kOrderPerLane; ++j) {
+            const int b = kOrderBuckets - 1 - (kOrderPerLane * lane + j);
+            c[j] = b >= 0 ? next[b] : 0u;
+            own += c[j];
+        }
+        unsigned incl = own;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const unsigned y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        unsigned run = incl - own;
+#pragma unroll
+        for (int j = 0; j < kOrderPerLane; ++j) {
+            const int b = kOrderBuckets - 1 - (kOrderPerLane * lane + j);
+            if (b >= 0) next[b] = run;
+            run += c[j];
+        }
+    }
+    __syncthreads();
+    for (int s = threadIdx.x; s < n; s += kOrderThreads) order[atomicAdd(&next[bucket[s]], 1u)] = s;
 }
 
 // The second pass of a split launch: one workgroup of kSegmentCombineWaves
@@ -182,59 +263,69 @@ constexpr int segment_sums_depth(int64_t waves, int cols) {
 template <int DEPTH, bool PARTS>
 static void launch_segment_sums_depth(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
                                       const int64_t *offsets, int64_t units, int parts, int cols, float *dst,
-                                      int32_t *tail_counts, hipStream_t stream) {
+                                      int32_t *tail_counts, const int32_t *order, hipStream_t stream) {
     if (vec4) {
         if (cols % (kWave * 4) == 0)
             segment_sums_kernel<4, true, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
-                                                                                   parts, cols, dst, tail_counts);
+                                                                                   parts, cols, dst, tail_counts, order);
         else
             segment_sums_kernel<4, false, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
-                                                                                    parts, cols, dst, tail_counts);
+                                                                                    parts, cols, dst, tail_counts, order);
     } else {
         if (cols % kWave == 0)
             segment_sums_kernel<1, true, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
-                                                                                   parts, cols, dst, tail_counts);
+                                                                                   parts, cols, dst, tail_counts, order);
         else
             segment_sums_kernel<1, false, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
-                                                                                    parts, cols, dst, tail_counts);
+                                                                                    parts, cols, dst, tail_counts, order);
     }
 }
 
 template <bool PARTS>
 static void launch_segment_units(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
                                  const int64_t *offsets, int64_t units, int parts, int cols, float *dst,
-                                 int32_t *tail_counts, hipStream_t stream) {
+                                 int32_t *tail_counts, const int32_t *order, hipStream_t stream) {
     switch (segment_sums_depth((int64_t)grid.x * grid.y, cols)) {
         case 4 * kSegmentDepth:
             launch_segment_sums_depth<4 * kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
-                                                                 parts, cols, dst, tail_counts, stream);
+                                                                 parts, cols, dst, tail_counts, order,
+                                                                 stream);
             break;
         case 2 * kSegmentDepth:
             launch_segment_sums_depth<2 * kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
-                                                                 parts, cols, dst, tail_counts, stream);
+                                                                 parts, cols, dst, tail_counts, order,
+                                                                 stream);
             break;
         default:
             launch_segment_sums_depth<kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
-                                                             parts, cols, dst, tail_counts, stream);
+                                                             parts, cols, dst, tail_counts, order, stream);
             break;
     }
 }
 
 hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, int64_t total_rows,
                                const int64_t *offsets, int64_t segments, int cols, float *out,
-                               int32_t *tail_counts, float *partial, hipStream_t stream) {
+                               int32_t *tail_counts, void *workspace, hipStream_t stream) {
     const dim3 grid(cfg.workgroups[0], cfg.workgroups[1]), block(cfg.workgroup_size[0]);
     const int parts = segment_sums_parts(segments, cols, total_rows);
-    float *dst = parts > 1 ? partial : out;  // what the row pass writes
-    const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
-                      (cols % 4 == 0);
     if (parts <= 1) {
+        const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                          (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (cols % 4 == 0);
+        int32_t *order = nullptr;
+        if (segment_sums_ordered(segments, cols, total_rows)) {
+            order = static_cast<int32_t *>(workspace);
+            segment_order_kernel<<<dim3(1), dim3(kOrderThreads), 0, stream>>>(offsets, segments, total_rows, order);
+            if (hipError_t e = hipGetLastError()) return e;
+        }
         launch_segment_units<false>(grid, block, vec4, x, total_rows, offsets, segments, 1, cols, out, tail_counts,
-                                    stream);
+                                    order, stream);
         return hipGetLastError();
     }
+    float *partial = static_cast<float *>(workspace);
+    const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                      (reinterpret_cast<uintptr_t>(partial) % 16 == 0) && (cols % 4 == 0);
     launch_segment_units<true>(grid, block, vec4, x, total_rows, offsets, segments * parts, parts, cols, partial,
-                               tail_counts, stream);
+                               tail_counts, nullptr, stream);
     if (hipError_t e = hipGetLastError()) return e;
     const dim3 cgrid((unsigned)grid_stride_groups(segments, kWave * kSegmentCombineWaves), cfg.workgroups[1]);
     segment_sums_combine_kernel<kSegmentCombineDepth>

@@ -308,6 +308,62 @@ def test_segment_sums_split_bad_offsets(loom, device):
     assert list(t) == [0, -1, 0, -1]
 
 
+# Many long segments of uneven length (2 to 2^15 segments averaging at least
+# 512 rows, at least 2^26 floats, not split) are first sorted by length so the
+# waves take them longest first: only the dispatch order changes, so every
+# output is still the in-order recurrence bit for bit.
+ORDER_CASES = [
+    (300, 1600, 256, [40000, 0, 17]),     # a long head, an empty and a short segment
+    (100, 1400, 1000, [30000, 1, 2]),     # four column blocks
+    (200, 2600, 256, [60000, 0]),         # 200 waves: just too many to split
+]
+
+
+def _ordered(loom, segments, cols, total):
+    return (2 <= segments <= 2 ** 15 and total // segments >= 512 and total * cols >= 2 ** 26
+            and _parts(loom, segments, cols, total) == 1)
+
+
+@pytest.mark.parametrize("segments,max_len,cols,head", ORDER_CASES)
+def test_segment_sums_longest_first_exact(loom, device, segments, max_len, cols, head):
+    tail = synth.segment_lengths(78, segments - len(head), max_len)
+    L = torch.cat([torch.tensor(head, dtype=torch.int64), tail])
+    off = synth.segment_offsets(L)
+    total = int(off[-1])
+    assert _ordered(loom, segments, cols, total)
+    x = synth.segment_rows(synth.SEGMENTS.seed, 0, total, cols)
+    dx, doff = x.to(device), off.to(device)
+    ref, rtails, _, _ = oracle.segment_sums(x.numpy(), off.numpy())
+    for noalloc in (False, True):
+        out, tails = loom.segment_sums(dx, doff, noalloc=noalloc)
+        assert np.array_equal(_np(out).view(np.uint32), ref.view(np.uint32)), noalloc
+        assert np.array_equal(_np(tails), rtails), noalloc
+
+
+def test_segment_sums_longest_first_bad_offsets(loom, device):
+    S, cols = 400, 256
+    L = synth.segment_lengths(79, S, 1400)
+    off = synth.segment_offsets(L)
+    total = int(off[-1])
+    assert _ordered(loom, S, cols, total)
+    x = synth.segment_rows(synth.SEGMENTS.seed, 0, total, cols)
+    bad = off.clone()
+    bad[10], bad[300] = bad[11] + 5, total + 3   # segment 9 ends past segment 10's end; 299 and 300 leave the rows
+    out, tails = loom.segment_sums(x.to(device), bad.to(device))
+    g, t = _np(out), _np(tails)
+    ok = np.ones(S, bool)
+    ok[[10, 299, 300]] = False        # decreasing [bad[10], bad[11]) and both ends past total_rows
+    ref, rtails, _, _ = oracle.segment_sums(x.numpy(), off.numpy())
+    assert np.all(np.isnan(g[~ok])) and np.all(t[~ok] == -1)
+    keep = np.flatnonzero(ok)
+    keep = keep[keep != 9]            # segment 9 now reads [off[9], off[11] + 5)
+    assert np.array_equal(g[keep].view(np.uint32), ref[keep].view(np.uint32))
+    assert np.array_equal(t[keep], rtails[keep])
+    b9, e9 = int(off[9]), int(off[11]) + 5
+    r9, rt9, _, _ = oracle.segment_sums(x.numpy()[b9:e9], np.array([0, e9 - b9]))
+    assert np.array_equal(g[9].view(np.uint32), r9[0].view(np.uint32)) and t[9] == rt9[0]
+
+
 def test_segment_sums_full_size(loom, device):
     S, cols = 16384, 256
     L = synth.segment_lengths(synth.SEGMENTS.seed, S, 4096)

@@ -1,8 +1,9 @@
 """loom_segment_sums_noalloc (the call for callers that cannot allocate),
 through the C ABI, against loom_segment_sums on the same inputs: two calls in
 a row, the second with a smaller input, in a split launch (partials in the
-library's static array) and in a single-pass launch; the results must be the
-same bits, and within the f32 tolerance of the oracle."""
+library's static array), in a longest-first launch (its order index there)
+and in a plain single-pass launch; the results must be the same bits, and
+within the f32 tolerance of the oracle."""
 import ctypes
 
 import numpy as np
@@ -33,18 +34,29 @@ def _call(lib, fn, x, off, cols):
     return out.cpu().numpy(), tails.cpu().numpy()
 
 
-@pytest.mark.parametrize("split", [True, False])
-def test_noalloc_matches_segment_sums(loom, device, split):
+# (lengths, cols) of the two calls; the second is smaller than the first
+# (fewer rows, segments and columns)
+CALLS = {
+    "split": [([100000, 5, 60000], 256), ([30000, 20000], 100)],
+    # 2 to 2^15 segments averaging >= 512 rows, >= 2^26 floats
+    "longest_first": [([1300, 0, 37, 900] * 80, 512), ([9, 1500] * 95, 480)],
+    "single": [([300, 0, 37, 900] * 100, 260), ([9, 400] * 150, 64)],
+}
+
+
+@pytest.mark.parametrize("mode", list(CALLS))
+def test_noalloc_matches_segment_sums(loom, device, mode):
     lib = loom.library()
     seg = loom.launch_config_lookup("segment_sums")
-    # the second call is smaller than the first (fewer rows, segments and columns)
-    shapes = ([[100000, 5, 60000], [30000, 20000]] if split else [[300, 0, 37, 900] * 100, [9, 400] * 150])
-    for lengths, cols in zip(shapes, (256, 100) if split else (260, 64)):
+    for lengths, cols in CALLS[mode]:
         L = torch.tensor(lengths, dtype=torch.int64)
         off = synth.segment_offsets(L)
         total = int(off[-1])
         parts = loom.launch_config_invoke(seg, [len(lengths), cols, total])["workgroups"][0] // len(lengths)
-        assert (parts > 1) == split, parts
+        assert (parts > 1) == (mode == "split"), parts
+        if mode != "split":
+            ordered = total // len(lengths) >= 512 and total * cols >= 2 ** 26
+            assert ordered == (mode == "longest_first"), (total, cols)
         x = synth.segment_rows(synth.SEGMENTS.seed, 0, total, cols)
         dx, doff = x.to(device), off.to(device)
         g_na, t_na = _call(lib, "loom_segment_sums_noalloc", dx, doff, cols)
