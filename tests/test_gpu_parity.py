@@ -437,6 +437,9 @@ I8_CASES = [
     # 2 (k = 4096), 4 (k = 16384 with few tiles, k = 32768) and 8 (k = 16384,
     # 513 tiles)
     (1000, 2048, 7), (100, 4096, 8), (300, 16384, 8), (50, 32768, 2), (8200, 16384, 3),
+    # the tile kernel and the row kernel with a single row, partial last
+    # tiles and thousands of tiles
+    (1, 2048, 2), (4111, 8192, 5), (12345, 6144, 15), (40000, 2048, 2), (333, 4096, 3),
     # 9-16 vectors with k a multiple of 1024 from 4096 to 8192: the row-streaming
     # kernel (one workgroup per CU walking 16-row tiles; 8197 rows give 513
     # tiles, so workgroups take two or three tiles each)
@@ -465,6 +468,7 @@ def test_i8_dequant_dot(loom, device, rows, k, batch):
 
 
 @pytest.mark.parametrize("rows,k,batch", [(70, 4096, 8), (70, 4096, 16), (70, 4096, 33), (70, 4096, 1),
+                                           (4111, 8192, 5), (90, 2048, 2), (70, 6144, 12),
                                            (70, 8192, 1), (70, 5000, 1), (70, 1536, 1), (70, 1028, 1),
                                            (130, 100, 1), (130, 12, 1)])
 def test_i8_unaligned_operands(loom, device, rows, k, batch):
