@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 INT8_PEAK_OPS = 5.0e15  # dense int8 MFMA, MI355X
 METRIC = "achieved HBM GB/s (and % of peak) for row-sum and int8 dequant-dot"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_row_sums_65536x4096.json")
-KERNEL_SOURCES = ("device_common.hpp", "internal.hpp", "row_sums.hip")
+KERNEL_SOURCES = ("device_common.hpp", "pipeline.hpp", "internal.hpp", "row_sums.hip")
 
 
 def kernel_source_hash() -> str:
