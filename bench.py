@@ -305,7 +305,7 @@ def main():
 
         # Few long segments (4 x 1,048,576 rows x 256 columns, 4 GiB): every
         # segment is split into parts summed in row order whose sums are added
-        # in part order (outside the step; parity in the tests).
+        # in a fixed order (outside the step; parity in the tests).
         S4 = 4
         off4 = torch.arange(S4 + 1, dtype=torch.int64, device=dev) * (1 << 20)
         x34 = synth.segment_matrix(synth.SEGMENTS.seed, S4 << 20, CS, device=dev)
