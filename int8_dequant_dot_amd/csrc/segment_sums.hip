@@ -141,27 +141,29 @@ __device__ __forceinline__ int length_bucket(int64_t begin, int64_t end, int64_t
 __global__ __launch_bounds__(kOrderThreads) void segment_order_kernel(const int64_t *__restrict__ offsets,
                                                                       int64_t segments, int64_t total_rows,
                                                                       int32_t *__restrict__ order) {
-    __shared__ unsigned next[kOrderBuckets];
+    // next[kOrderBuckets + lane] are spare counters for the slots past the
+    // last segment (one per lane, so they never contend), so the batches
+    // below run without branches
+    __shared__ unsigned next[kOrderBuckets + kWave];
     __shared__ uint8_t bucket[kSegmentOrderMaxSegments];
     const int n = (int)min(segments, kSegmentOrderMaxSegments);
-    for (int b = threadIdx.x; b < kOrderBuckets; b += kOrderThreads) next[b] = 0;
+    const int spare = kOrderBuckets + (int)(threadIdx.x & (kWave - 1));
+    for (int b = threadIdx.x; b < kOrderBuckets + kWave; b += kOrderThreads) next[b] = 0;
     __syncthreads();
     for (int base = 0; base < n; base += kOrderThreads * kOrderBatch) {
         int64_t begin[kOrderBatch], end[kOrderBatch];
 #pragma unroll
         for (int j = 0; j < kOrderBatch; ++j) {
-            const int s = base + j * kOrderThreads + (int)threadIdx.x;
-            begin[j] = s < n ? offsets[s] : 0;
-            end[j] = s < n ? offsets[s + 1] : 0;
+            const int s = min(base + j * kOrderThreads + (int)threadIdx.x, n - 1);
+            begin[j] = offsets[s];
+            end[j] = offsets[s + 1];
         }
 #pragma unroll
         for (int j = 0; j < kOrderBatch; ++j) {
             const int s = base + j * kOrderThreads + (int)threadIdx.x;
-            if (s < n) {
-                const int k = length_bucket(begin[j], end[j], total_rows);
-                bucket[s] = (uint8_t)k;
-                atomicAdd(&next[k], 1u);
-            }
+            const int k = s < n ? length_bucket(begin[j], end[j], total_rows) : spare;
+            if (s < n) bucket[s] = (uint8_t)k;
+            atomicAdd(&next[k], 1u);
         }
     }
     __syncthreads();
@@ -192,7 +194,22 @@ __global__ __launch_bounds__(kOrderThreads) void segment_order_kernel(const int6
         }
     }
     __syncthreads();
-    for (int s = threadIdx.x; s < n; s += kOrderThreads) order[atomicAdd(&next[bucket[s]], 1u)] = s;
+    for (int base = 0; base < n; base += kOrderThreads * kOrderBatch) {
+        int k[kOrderBatch];
+        unsigned pos[kOrderBatch];
+#pragma unroll
+        for (int j = 0; j < kOrderBatch; ++j) {
+            const int s = base + j * kOrderThreads + (int)threadIdx.x;
+            k[j] = s < n ? bucket[min(s, n - 1)] : spare;
+        }
+#pragma unroll
+        for (int j = 0; j < kOrderBatch; ++j) pos[j] = atomicAdd(&next[k[j]], 1u);
+#pragma unroll
+        for (int j = 0; j < kOrderBatch; ++j) {
+            const int s = base + j * kOrderThreads + (int)threadIdx.x;
+            if (s < n) order[pos[j]] = s;
+        }
+    }
 }
 
 // The second pass of a split launch: one workgroup of kSegmentCombineWaves
