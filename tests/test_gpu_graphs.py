@@ -6,7 +6,10 @@ kernels only (no host synchronisation, allocation or memset on the stream),
 and no kernel depends on state left by an earlier launch.  Between replays
 the outputs are poisoned and unrelated eager work runs on the same stream.
 One case per kernel variant (narrow, tiled and long-row row sums; GEMV and
-all three MFMA kernels; one-output and four-output packed dot; ...).
+all three MFMA kernels; one-output and four-output packed dot; ...).  The
+segment sums' split and longest-first launches, whose workspace the
+allocating call takes from the stream-ordered allocator, are captured
+through the no-alloc entry point, the one meant for graphs.
 """
 import numpy as np
 import pytest
@@ -46,6 +49,17 @@ def _cases(loom, dev):
         so = torch.empty(7, cols, device=dev)
         st = torch.empty(7, dtype=torch.int32, device=dev)
         c[f"segment_sums_{cols}"] = (lambda xs=xs, off=off, so=so, st=st: loom.segment_sums(xs, off, so, st))
+    # few long segments (split: partials in the static array) and many long
+    # uneven ones over >= 2^26 floats (longest first: the order index there)
+    for name, L, cols in (("split", torch.tensor([40000, 3, 30000], dtype=torch.int64), 256),
+                          ("ordered", torch.cat([torch.tensor([40000, 0], dtype=torch.int64),
+                                                 synth.segment_lengths(78, 298, 1600)]), 256)):
+        off = synth.segment_offsets(L).to(dev)
+        xs = synth.segment_rows(synth.SEGMENTS.seed, 0, int(off[-1]), cols, dev)
+        so = torch.empty(L.numel(), cols, device=dev)
+        st = torch.empty(L.numel(), dtype=torch.int32, device=dev)
+        c[f"segment_sums_noalloc_{name}"] = (lambda xs=xs, off=off, so=so, st=st:
+                                             loom.segment_sums(xs, off, so, st, noalloc=True))
     for batch in (1, 8, 16, 40):
         w = loom.pack_int8(synth.i8_rows(5, synth.S_W, 0, 300, 8192, dev))
         v = loom.pack_int8(synth.i8_rows(5, synth.S_X, 0, batch, 8192, dev))
@@ -85,7 +99,8 @@ def _cases(loom, dev):
 
 
 CASE_NAMES = ["copy_f32", "row_sum_tiles", "row_sums_narrow", "row_sums_tiled", "row_sums_long",
-              "segment_sums_256", "segment_sums_300", "i8_dequant_dot_b1", "i8_dequant_dot_b8", "i8_dequant_dot_b16",
+              "segment_sums_256", "segment_sums_300", "segment_sums_noalloc_split", "segment_sums_noalloc_ordered",
+              "i8_dequant_dot_b1", "i8_dequant_dot_b8", "i8_dequant_dot_b16",
               "i8_dequant_dot_b40", "i8_dequant_dot_b64_5000", "i8_dequant_dot_b4_k1024",
               "packed_dot_2048", "packed_dot_65856", "sum_guarded_rows", "routed_combine"]
 
