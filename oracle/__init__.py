@@ -23,7 +23,7 @@ CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-st
 
 
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (the checker is built, not used, by this call)."""
+    """Compile the oracle with gcc (this call builds it and runs nothing of it)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
