@@ -213,17 +213,19 @@ __global__ __launch_bounds__(kOrderThreads) void segment_order_kernel(const int6
 }
 
 // The second pass of a split launch: one workgroup of kSegmentCombineWaves
-// waves per segment and 256-column block, a lane per column.  Wave w adds,
-// in part order, the partials of its contiguous run of parts -- parts
-// w * R .. w * R + R - 1, R = ceil(P / kSegmentCombineWaves) -- with the
-// partials read ahead, and out[s][c] is the sum of the run sums in run order,
-// all in f32 from +0.0: a fixed association of the P part sums, so a call
-// gives the same bits every time.  A segment with bad offsets has NaN
-// partials, so its outputs stay NaN.
-template <int DEPTH>
+// waves per segment and 256-column block, a lane per VEC adjacent columns
+// (VEC = 4: one 1 KiB load per part row of the block).  Wave w adds, in part
+// order, the partials of its contiguous run of parts -- parts w * R .. w * R
+// + R - 1, R = ceil(P / kSegmentCombineWaves) -- with the partials read ahead,
+// and out[s][c] is the sum of the run sums in run order, all in f32 from
+// +0.0: a fixed association of the P part sums, so a call gives the same bits
+// every time.  A segment with bad offsets has NaN partials, so its outputs
+// stay NaN.
+template <int VEC, int DEPTH>
 __global__ __launch_bounds__(kWave * kSegmentCombineWaves) void segment_sums_combine_kernel(
     const float *__restrict__ partial, int64_t segments, int parts, int cols, float *__restrict__ out) {
-    __shared__ float run[kSegmentCombineWaves][kWave];
+    typedef typename seg_vec<VEC>::type V;
+    __shared__ V run[kSegmentCombineWaves][kWave];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int per = (parts + kSegmentCombineWaves - 1) / kSegmentCombineWaves;
@@ -232,25 +234,26 @@ __global__ __launch_bounds__(kWave * kSegmentCombineWaves) void segment_sums_com
     const int block_first = blockIdx.y * kSegmentBlockCols;
     const int block_end = min(cols, block_first + kSegmentBlockCols);
     for (int64_t s = blockIdx.x; s < segments; s += gridDim.x) {
-        for (int c0 = block_first; c0 < block_end; c0 += kWave) {
-            const int c = c0 + lane;
-            const bool active = c < block_end;
-            const float *pp = partial + (s * parts + first) * cols + (active ? c : block_first);
-            float acc = 0.0f;
-            pipelined<DEPTH, float>(
+        for (int c0 = block_first; c0 < block_end; c0 += kWave * VEC) {
+            const int c = c0 + lane * VEC;
+            const bool active = c < block_end;  // VEC = 4: cols % 4 == 0, so a group is wholly in or out
+            const V *pp = reinterpret_cast<const V *>(partial + (s * parts + first) * cols + (active ? c : block_first));
+            const int stride = cols / VEC;
+            V acc = V{};
+            pipelined<DEPTH, V, true>(  // the straight drain: no copies of the ring at this register budget
                 n,
                 [&]() {
-                    const float v = *pp;
-                    pp += cols;
+                    const V v = *pp;
+                    pp += stride;
                     return v;
                 },
-                [&](float v) { acc = acc + v; });
+                [&](V v) { acc = acc + v; });
             run[wave][lane] = acc;
             __syncthreads();
             if (wave == 0) {
-                float sum = 0.0f;
+                V sum = V{};
                 for (int v = 0; v < kSegmentCombineWaves; ++v) sum = sum + run[v][lane];
-                if (active) out[s * cols + c] = sum;
+                if (active) *reinterpret_cast<V *>(out + s * cols + c) = sum;
             }
             __syncthreads();  // run[] is rewritten next
         }
@@ -270,7 +273,10 @@ __global__ __launch_bounds__(kWave * kSegmentCombineWaves) void segment_sums_com
 #define LOOM_SEGMENT_SUMS_DEPTH 8
 #endif
 constexpr int kSegmentDepth = LOOM_SEGMENT_SUMS_DEPTH;
-constexpr int kSegmentCombineDepth = 8;
+#ifndef LOOM_SEGMENT_COMBINE_DEPTH
+#define LOOM_SEGMENT_COMBINE_DEPTH 8
+#endif
+constexpr int kSegmentCombineDepth = LOOM_SEGMENT_COMBINE_DEPTH;  // part rows in flight per wave of the combine
 constexpr int segment_sums_depth(int64_t waves, int cols) {
     const int by_waves = waves <= 256 ? 4 * kSegmentDepth : waves <= 1024 ? 2 * kSegmentDepth : kSegmentDepth;
     const int by_width = cols <= 64 ? 4 * kSegmentDepth : cols <= 128 ? 2 * kSegmentDepth : kSegmentDepth;
@@ -345,8 +351,13 @@ hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, in
                                tail_counts, nullptr, stream);
     if (hipError_t e = hipGetLastError()) return e;
     const dim3 cgrid((unsigned)grid_stride_groups(segments, kWave * kSegmentCombineWaves), cfg.workgroups[1]);
-    segment_sums_combine_kernel<kSegmentCombineDepth>
-        <<<cgrid, dim3(kWave * kSegmentCombineWaves), 0, stream>>>(partial, segments, parts, cols, out);
+    const dim3 cblock(kWave * kSegmentCombineWaves);
+    if (vec4 && reinterpret_cast<uintptr_t>(out) % 16 == 0)
+        segment_sums_combine_kernel<4, kSegmentCombineDepth><<<cgrid, cblock, 0, stream>>>(partial, segments, parts,
+                                                                                          cols, out);
+    else
+        segment_sums_combine_kernel<1, kSegmentCombineDepth><<<cgrid, cblock, 0, stream>>>(partial, segments, parts,
+                                                                                          cols, out);
     return hipGetLastError();
 }
 
