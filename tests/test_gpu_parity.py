@@ -364,6 +364,53 @@ def test_segment_sums_longest_first_bad_offsets(loom, device):
     assert np.array_equal(g[9].view(np.uint32), r9[0].view(np.uint32)) and t[9] == rt9[0]
 
 
+def _alternating(segments, short, long, extra=()):
+    L = torch.tensor([short, long] * (segments // 2) + list(extra), dtype=torch.int64)
+    return L
+
+
+# Both sides of every threshold that picks a segment-sum launch form: the
+# split reading (fewer than 192 waves and at least 1024 rows per segment on
+# average) and longest-first order (2 to 2^15 segments, at least 512 rows on
+# average, at least 2^26 floats).  Split launches are checked within the f32
+# tolerance and for the same bits on a second call; every other launch is the
+# in-order recurrence bit for bit.
+BOUNDARY_CASES = [
+    ("split", lambda: torch.full((191,), 1100, dtype=torch.int64), 256),        # 191 waves
+    ("in_order", lambda: torch.full((192,), 1100, dtype=torch.int64), 256),     # 192 waves
+    ("split", lambda: torch.full((8,), 1024, dtype=torch.int64), 256),          # 1024 rows on average
+    ("in_order", lambda: torch.full((8,), 1023, dtype=torch.int64), 256),       # 1023
+    ("in_order", lambda: _alternating(2 ** 15, 256, 768), 4),                   # 2^15 segments: longest first
+    ("in_order", lambda: _alternating(2 ** 15, 256, 768, [512]), 4),            # 2^15 + 1: index order
+    ("in_order", lambda: _alternating(4096, 254, 768), 64),                     # 511 rows on average
+    ("in_order", lambda: _alternating(4096, 256, 768), 64),                     # 512
+    ("in_order", lambda: _alternating(4096, 256, 768), 31),                     # 2^26 - 2^21 floats
+    ("in_order", lambda: _alternating(4096, 256, 768), 32),                     # 2^26
+]
+
+
+@pytest.mark.parametrize("form,lengths,cols", BOUNDARY_CASES,
+                         ids=[f"{i}-{c[0]}-{c[2]}cols" for i, c in enumerate(BOUNDARY_CASES)])
+def test_segment_sums_form_boundaries(loom, device, form, lengths, cols):
+    L = lengths()
+    off = synth.segment_offsets(L)
+    total = int(off[-1])
+    S = L.numel()
+    assert (_parts(loom, S, cols, total) > 1) == (form == "split")
+    x = synth.segment_rows(synth.SEGMENTS.seed, 0, total, cols)
+    dx, doff = x.to(device), off.to(device)
+    out, tails = loom.segment_sums(dx, doff)
+    g = _np(out)
+    ref, rtails, d, a = oracle.segment_sums(x.numpy(), off.numpy())
+    assert np.array_equal(_np(tails), rtails)
+    if form == "split":
+        assert_sum_close(g, ref, d, a, what=f"split boundary {S}x{cols}")
+        again, _ = loom.segment_sums(dx, doff)
+        assert np.array_equal(_np(again).view(np.uint32), g.view(np.uint32))
+    else:
+        assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
 def test_segment_sums_full_size(loom, device):
     S, cols = 16384, 256
     L = synth.segment_lengths(synth.SEGMENTS.seed, S, 4096)
