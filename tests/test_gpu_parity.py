@@ -478,6 +478,10 @@ I8_CASES = [
     (3, 516, 1), (200, 528, 1), (200, 768, 1), (9, 1028, 1), (33, 1040, 1), (77, 1280, 1), (100, 2112, 1),
     (3000, 1536, 1), (257, 2560, 1), (41, 4092, 1), (19, 4100, 1), (130, 4608, 1), (23, 5124, 1),
     (5, 8704, 1), (40, 12804, 1), (6, 16896, 1),
+    # both sides of each form's edge: the wide form at 6 and 7 KiB (5 KiB and
+    # 9 KiB rows walk row by row), the grouped form up to 12284 bytes (12288
+    # is whole records)
+    (33, 6144, 1), (21, 7168, 1), (12, 5120, 1), (3, 9216, 1), (9, 12284, 1), (10, 12288, 1),
     (3, 64, 2), (15, 256, 3), (16, 260, 8), (17, 1000, 8), (100, 8192, 8), (33, 64, 16), (40, 512, 17),
     (20, 1024, 32), (18, 320, 33), (16, 4096, 64), (1, 4, 2), (31, 8, 5),
     # the tile kernel's k split: 1 wave per tile (k <= 2048, several records),
