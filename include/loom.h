@@ -22,14 +22,20 @@
  *    (LOOM_ERR_ALIGN) are checked.
  *  - Data pointers are device pointers (HIP allocations of the current device,
  *    e.g. a torch tensor's data_ptr()).  The caller owns all memory.  The
- *    library allocates no device memory and keeps no pointer after returning.
+ *    library keeps no pointer after returning and allocates no device memory,
+ *    except loom_segment_sums in its split and longest-first launches, whose
+ *    workspace comes from HIP's stream-ordered allocator (see there;
+ *    loom_segment_sums_noalloc never allocates).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *    asynchronously on it; outputs are ready once the stream has reached the
  *    enqueued work.  A device-side fault is reported by later HIP calls, not
  *    by the return code; LOOM_ERR_DEVICE means the launch itself was refused
  *    (the thread's last HIP error is cleared before each launch, so an error
  *    left by an earlier, unrelated HIP call is never reported as this one).
- *  - Calls are thread-safe: the only shared state is an immutable table.
+ *  - Calls are thread-safe: the shared state is an immutable table and, for
+ *    loom_segment_sums_noalloc, a lock-guarded per-device address cache and
+ *    the static device array (calls of it that overlap on one GPU race; see
+ *    there).
  *  - Matrices are row-major.  Packed int8: an int32 word j of a row holds the
  *    elements 4j..4j+3, element 4j+b in byte b (little-endian), two's
  *    complement -- exactly the bytes of an int8 array viewed as int32.
