@@ -64,6 +64,11 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t
 
 
+def _waves(cfg) -> int:
+    """Waves along a launch's first grid axis (a split segment-sum launch runs one per part)."""
+    return cfg["workgroups"][0] * cfg["workgroup_size"][0] // 64
+
+
 def graph_us(fn, reps: int):
     """Device time of one call of `fn` (a launch-bound entry point), as
     (microseconds per call in a HIP graph of `reps` back-to-back calls,
@@ -329,8 +334,8 @@ def main():
             "bytes": bytes34, "us": round(ms34 * 1e3, 1), "GB/s": round(bytes34 / (ms34 * 1e-3) / 1e9, 1),
             "frac_of_peak": round(bytes34 / (ms34 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "us_median": round(reps34[REPS // 2] * 1e3, 1), "us_min": round(reps34[0] * 1e3, 1),
-            "parts_per_segment": loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"),
-                                                           [S4, CS, S4 << 20])["workgroups"][0] // S4}
+            "parts_per_segment": _waves(loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"),
+                                                                  [S4, CS, S4 << 20])) // S4}
         log(f"few long segments: {parts['segment_sums_4x1M']}")
         del x34, out34
         torch.cuda.empty_cache()

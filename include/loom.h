@@ -176,11 +176,14 @@ int loom_row_sums(const float *x, int64_t rows, int64_t cols, int64_t row_stride
  * and the segments average at least 1024 rows (total_rows / segments), each *
  * segment is split into P contiguous parts of at least 512 rows on average  *
  * (P * segments * ceil(cols / 256) <= 4096), each part summed in row order, *
- * and the P part sums added in a fixed order (contiguous runs of           *
- * ceil(P / 16) parts in part order, then the run sums in run order): the    *
- * same bits on every call, within 1e-5 * sum|x| of the in-order sum.  The   *
- * partials (4 * segments * P * cols bytes, at most 4 MiB) are then taken    *
- * from HIP's stream-ordered allocator on `stream` (hipMallocAsync /         *
+ * and the part sums added in a fixed order.  With cols <= 512 and P >= 16,  *
+ * P is a multiple of 8 and the sums of each run of 8 consecutive parts are  *
+ * added in part order, leaving n = P / 8 partials per segment; otherwise    *
+ * the n = P part sums are the partials.  The n partials are added as        *
+ * contiguous groups of ceil(n / 16) in order, then the group sums in group  *
+ * order: the same bits on every call, within 1e-5 * sum|x| of the in-order  *
+ * sum.  The partials (4 * segments * n * cols bytes, at most 4 MiB) are     *
+ * taken from HIP's stream-ordered allocator on `stream` (hipMallocAsync /   *
  * hipFreeAsync).  A launch that is not split, of 2 to 2^15 segments         *
  * averaging at least 512 rows and of at least 2^26 floats, first sorts the  *
  * segments by length (a one-workgroup pass) so its waves take them longest  *

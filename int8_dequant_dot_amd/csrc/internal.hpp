@@ -87,14 +87,15 @@ constexpr int kSegmentBlockCols = 256;
 // 2 * kSegmentSplitMinRows rows splits every segment into P contiguous parts
 // of at least kSegmentSplitMinRows rows on average, P * waves at most
 // kSegmentSplitWaves: each part is summed in row order into a partial, and a
-// second pass adds each segment's P partials in a fixed order (contiguous
-// runs of parts in part order, then the runs in run order; one
+// second pass adds each segment's partials in a fixed order (contiguous
+// groups of partials in order, then the groups in group order; one
 // kSegmentCombineWaves-wave workgroup per segment and column block).  The
-// partials need segments * P * cols floats, at most kSegmentSplitWaves * 256
-// (4 MiB).  Returns P, or 1 for the single pass (every column's sum in row
-// order).  Over 4 GiB of 256-column rows (one MI355X), the single pass took
-// 75.4 ms for one segment, 19.0 ms for 4, 1366 us for 64, 704 us for 160 and
-// 606 us for 200 segments; split, 681, 650, 652, 657 and 637 us.
+// partials need at most segments * P * cols floats, at most
+// kSegmentSplitWaves * 256 (4 MiB).  Returns P, or 1 for the single pass
+// (every column's sum in row order).  Over 4 GiB of 256-column rows (one
+// MI355X), the single pass took 75.4 ms for one segment, 19.0 ms for 4,
+// 1366 us for 64, 704 us for 160 and 606 us for 200 segments; split, 681,
+// 650, 652, 657 and 637 us.
 #ifndef LOOM_SEGMENT_SPLIT_MIN_WAVES
 #define LOOM_SEGMENT_SPLIT_MIN_WAVES 192
 #endif
@@ -103,13 +104,44 @@ constexpr int kSegmentCombineWaves = 16;
 constexpr int64_t kSegmentSplitWaves = 4096;
 constexpr int64_t kSegmentSplitMinRows = 512;
 constexpr int64_t kSegmentSplitMaxBytes = kSegmentSplitWaves * kSegmentBlockCols * 4;
+// Runs.  Rows of at most kSegmentRunMaxCols columns split into at least
+// 2 * kSegmentRunWaves parts take P a multiple of kSegmentRunWaves and group
+// the parts in runs of kSegmentRunWaves consecutive parts, one workgroup per
+// run whose waves add their part sums in part order through LDS: the
+// partials (and the second pass's reads) shrink to one run sum per run, a
+// single segment of 4 M rows leaving 512 KiB for one CU to add instead of
+// 4 MiB.  Over 4 GiB (one MI355X), runs of 8 took 643 us for one 256-column
+// segment (689 us without), 641 us for 4 (659), 640 us for 128 (648) and
+// 642 us for one 512-column segment (669); on 1024-column rows they lost
+// (676 vs 640 us for one segment, 696 vs 654 for 16), as did runs of 16
+// there, so wider rows keep one partial per part.
+#ifndef LOOM_SEGMENT_RUN_WAVES
+#define LOOM_SEGMENT_RUN_WAVES 8
+#endif
+constexpr int kSegmentRunWaves = LOOM_SEGMENT_RUN_WAVES;
+constexpr int64_t kSegmentRunMaxCols = 2 * kSegmentBlockCols;
+constexpr bool segment_runs_fit(int64_t p, int64_t cols) {
+    return kSegmentRunWaves > 1 && cols <= kSegmentRunMaxCols && p >= 2 * kSegmentRunWaves;
+}
 constexpr int segment_sums_parts(int64_t segments, int64_t cols, int64_t total_rows) {
     const int64_t blocks = cols > 0 ? (cols + kSegmentBlockCols - 1) / kSegmentBlockCols : 1;
     if (segments <= 0 || cols <= 0 || segments * blocks >= kSegmentSplitMinWaves) return 1;
     const int64_t by_waves = kSegmentSplitWaves / (segments * blocks);
     const int64_t by_rows = total_rows / segments / kSegmentSplitMinRows;
-    const int64_t p = by_waves < by_rows ? by_waves : by_rows;
+    int64_t p = by_waves < by_rows ? by_waves : by_rows;
+    if (segment_runs_fit(p, cols)) p -= p % kSegmentRunWaves;  // whole runs
     return p >= 2 ? (int)p : 1;
+}
+// Runs per segment of a split launch (0: no runs, one partial per part).
+constexpr int segment_sums_runs(int64_t segments, int64_t cols, int64_t total_rows) {
+    const int p = segment_sums_parts(segments, cols, total_rows);
+    return segment_runs_fit(p, cols) ? p / kSegmentRunWaves : 0;
+}
+// Partial sums per segment that the second pass adds: one per run, else one
+// per part.
+constexpr int segment_sums_partials(int64_t segments, int64_t cols, int64_t total_rows) {
+    const int r = segment_sums_runs(segments, cols, total_rows);
+    return r > 0 ? r : segment_sums_parts(segments, cols, total_rows);
 }
 // Many long segments of uneven length: a single pass over at least
 // kSegmentOrderMinFloats floats of 2 to kSegmentOrderMaxSegments segments
@@ -141,7 +173,8 @@ constexpr bool segment_sums_ordered(int64_t segments, int64_t cols, int64_t tota
 // kSegmentSplitMaxBytes either way).
 constexpr int64_t segment_sums_workspace_bytes(int64_t segments, int64_t cols, int64_t total_rows) {
     const int p = segment_sums_parts(segments, cols, total_rows);
-    return p > 1 ? segments * p * cols * 4 : segment_sums_ordered(segments, cols, total_rows) ? segments * 4 : 0;
+    return p > 1 ? segments * segment_sums_partials(segments, cols, total_rows) * cols * 4
+                 : segment_sums_ordered(segments, cols, total_rows) ? segments * 4 : 0;
 }
 
 // Blocking of the int8 kernels.  One vector always runs a v_dot4 GEMV, in

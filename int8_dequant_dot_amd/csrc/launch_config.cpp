@@ -68,14 +68,21 @@ int geo_row_sums(const int64_t *w, loom_launch_config *c) {
 }
 
 // segment_sums(segments, cols, total_rows): one wave per segment -- or, for a
-// few long segments, per part of a segment (segment_sums_parts) -- and block
-// of kSegmentBlockCols columns (at least one block, which also writes the
-// segment's tail count when there are no columns); past 2^26 - 1 units each
-// wave takes every grid.x-th unit.  A split launch is followed by a pass of
-// one wave per segment and block that adds the parts.
+// few long segments, per part of a segment (segment_sums_parts), the parts
+// grouped in workgroups of kSegmentRunWaves waves per run when there are
+// runs (segment_sums_runs) -- and block of kSegmentBlockCols columns (at
+// least one block, which also writes the segment's tail count when there are
+// no columns); past the grid's work-item limit each workgroup takes every
+// grid.x-th unit.  A split launch is followed by a pass of one workgroup per
+// segment and block that adds the partials.
 int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 0) return LOOM_ERR_RANGE;
     const int64_t blocks = w[1] > 0 ? ceil_div(w[1], kSegmentBlockCols) : 1;
+    if (const int runs = segment_sums_runs(w[0], w[1], w[2])) {  // LDS: the run's part sums of one column block
+        const int64_t size = kSubgroupSize * kSegmentRunWaves;
+        return set2(c, grid_stride_groups(w[0] * runs, size), blocks, (uint32_t)size,
+                    (uint32_t)(kSegmentRunWaves * kSegmentBlockCols * 4));
+    }
     const int64_t units = w[0] * segment_sums_parts(w[0], w[1], w[2]);
     return set2(c, grid_stride_groups(units, kSubgroupSize), blocks, kSubgroupSize, 0);
 }

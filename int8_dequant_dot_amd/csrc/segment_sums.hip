@@ -63,31 +63,41 @@ template <> struct seg_vec<4> { typedef float4v type; };
 // segment u / P, the rows [len * p / P, len * (p + 1) / P) of the segment,
 // and the wave writes its partial column sums to dst = partial[u][cols];
 // segment_sums_combine_kernel then adds the P partials of each segment.
-// Otherwise unit u is segment order[u] (longest first, segment_sums_ordered)
-// or segment u, and dst = out[s][cols].
+// With RUN > 1 waves per workgroup (segment_sums_runs), unit u is run u mod
+// R of segment u / R, wave w sums part RUN * (u mod R) + w, and the waves'
+// part sums are added in part order through LDS into dst = partial[u][cols]
+// (the segment's R partials then go to the second pass).  Otherwise unit u is
+// segment order[u] (longest first, segment_sums_ordered) or segment u, and
+// dst = out[s][cols].
 // ----------------------------------------------------------------------------
-template <int VEC, bool FULL, int DEPTH, bool PARTS>
-__global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__restrict__ x, int64_t total_rows,
-                                                             const int64_t *__restrict__ offsets, int64_t units,
-                                                             int parts, int cols, float *__restrict__ dst,
-                                                             int32_t *__restrict__ tail_counts,
-                                                             const int32_t *__restrict__ order) {
+template <int VEC, bool FULL, int DEPTH, bool PARTS, int RUN = 1>
+__global__ __launch_bounds__(kWave * RUN) void segment_sums_kernel(const float *__restrict__ x, int64_t total_rows,
+                                                                   const int64_t *__restrict__ offsets,
+                                                                   int64_t units, int parts, int cols,
+                                                                   float *__restrict__ dst,
+                                                                   int32_t *__restrict__ tail_counts,
+                                                                   const int32_t *__restrict__ order) {
+    static_assert(RUN == 1 || PARTS, "runs group the parts of a split launch");
     typedef typename seg_vec<VEC>::type V;
     constexpr int kBlock = kWave * VEC;
+    __shared__ V run_sums[RUN][RUN > 1 ? kBlock : 1];  // a column group's part sums, one row per wave
     const int lane = lane_id();
+    const int wave = RUN > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)) : 0;
+    const int runs = parts / RUN;  // units per segment with RUN > 1
     const int block_first = blockIdx.y * kSegmentBlockCols;
     const int block_end = min(cols, block_first + kSegmentBlockCols);
-    // one unit per wave; past the grid's work-item limit, every grid.x-th unit
+    // one unit per workgroup; past the grid's work-item limit, every grid.x-th unit
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-        const int64_t s = PARTS ? u / parts : order ? (int64_t)order[u] : u;
-        const int p = PARTS ? (int)(u - s * parts) : 0;
+        const int64_t s = RUN > 1 ? u / runs : PARTS ? u / parts : order ? (int64_t)order[u] : u;
+        const int p = RUN > 1 ? (int)(u - s * runs) * RUN + wave : PARTS ? (int)(u - s * parts) : 0;
         const int64_t begin = offsets[s];
         const int64_t end = offsets[s + 1];
         float *o = dst + (PARTS ? u : s) * cols;
         const bool writes_tail = p == 0 && blockIdx.y == 0 && tail_counts;
 
-        if (!(begin >= 0 && begin <= end && end <= total_rows)) {
-            for (int c = block_first + lane; c < block_end; c += kWave) o[c] = __builtin_nanf("");
+        if (!(begin >= 0 && begin <= end && end <= total_rows)) {  // the same in every wave of a run
+            if (wave == 0)
+                for (int c = block_first + lane; c < block_end; c += kWave) o[c] = __builtin_nanf("");
             if (lane == 0 && writes_tail) tail_counts[s] = -1;
             continue;
         }
@@ -104,7 +114,9 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
             const float *rp = x + first * cols + cb;
             const int lane_col = active ? lane * VEC : -cb;  // inactive lanes read the row's first columns
             V acc = V(0.0f);
-            pipelined<DEPTH, V>(
+            // the straight drain for runs: no copies of the ring at the register
+            // budget of a 16-wave workgroup
+            pipelined<DEPTH, V, (RUN > 1)>(
                 count,
                 [&]() {
                     const V v = load_stream(reinterpret_cast<const V *>(rp + lane_col));
@@ -112,7 +124,18 @@ __global__ __launch_bounds__(kWave) void segment_sums_kernel(const float *__rest
                     return v;
                 },
                 [&](V v) { acc += v; });
-            if (active) *reinterpret_cast<V *>(o + c) = acc;
+            if constexpr (RUN > 1) {
+                run_sums[wave][lane] = acc;
+                __syncthreads();
+                if (wave == 0) {
+                    V sum = V(0.0f);
+                    for (int w = 0; w < RUN; ++w) sum += run_sums[w][lane];
+                    if (active) *reinterpret_cast<V *>(o + c) = sum;
+                }
+                __syncthreads();  // run_sums is rewritten next
+            } else {
+                if (active) *reinterpret_cast<V *>(o + c) = acc;
+            }
         }
     }
 }
@@ -283,46 +306,55 @@ constexpr int segment_sums_depth(int64_t waves, int cols) {
     return by_waves > by_width ? by_waves : by_width;
 }
 
-template <int DEPTH, bool PARTS>
+template <int DEPTH, bool PARTS, int RUN>
 static void launch_segment_sums_depth(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
                                       const int64_t *offsets, int64_t units, int parts, int cols, float *dst,
                                       int32_t *tail_counts, const int32_t *order, hipStream_t stream) {
+#define LOOM_SEGMENT_LAUNCH(VEC, FULL)                                                                      \
+    segment_sums_kernel<VEC, FULL, DEPTH, PARTS, RUN><<<grid, block, 0, stream>>>(x, total_rows, offsets, units, \
+                                                                                 parts, cols, dst, tail_counts, \
+                                                                                 order)
     if (vec4) {
         if (cols % (kWave * 4) == 0)
-            segment_sums_kernel<4, true, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
-                                                                                   parts, cols, dst, tail_counts, order);
+            LOOM_SEGMENT_LAUNCH(4, true);
         else
-            segment_sums_kernel<4, false, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
-                                                                                    parts, cols, dst, tail_counts, order);
+            LOOM_SEGMENT_LAUNCH(4, false);
     } else {
         if (cols % kWave == 0)
-            segment_sums_kernel<1, true, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
-                                                                                   parts, cols, dst, tail_counts, order);
+            LOOM_SEGMENT_LAUNCH(1, true);
         else
-            segment_sums_kernel<1, false, DEPTH, PARTS><<<grid, block, 0, stream>>>(x, total_rows, offsets, units,
-                                                                                    parts, cols, dst, tail_counts, order);
+            LOOM_SEGMENT_LAUNCH(1, false);
     }
+#undef LOOM_SEGMENT_LAUNCH
 }
 
-template <bool PARTS>
+// The read-ahead depth follows the launch's wave count and the row width; a
+// run's 16 waves keep the base depth (a deeper ring of 4-wide records does not
+// fit their register budget).
+template <bool PARTS, int RUN = 1>
 static void launch_segment_units(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
                                  const int64_t *offsets, int64_t units, int parts, int cols, float *dst,
                                  int32_t *tail_counts, const int32_t *order, hipStream_t stream) {
-    switch (segment_sums_depth((int64_t)grid.x * grid.y, cols)) {
-        case 4 * kSegmentDepth:
-            launch_segment_sums_depth<4 * kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
-                                                                 parts, cols, dst, tail_counts, order,
-                                                                 stream);
-            break;
-        case 2 * kSegmentDepth:
-            launch_segment_sums_depth<2 * kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
-                                                                 parts, cols, dst, tail_counts, order,
-                                                                 stream);
-            break;
-        default:
-            launch_segment_sums_depth<kSegmentDepth, PARTS>(grid, block, vec4, x, total_rows, offsets, units,
-                                                             parts, cols, dst, tail_counts, order, stream);
-            break;
+    if constexpr (RUN > 1) {
+        launch_segment_sums_depth<kSegmentDepth, PARTS, RUN>(grid, block, vec4, x, total_rows, offsets, units, parts,
+                                                             cols, dst, tail_counts, order, stream);
+    } else {
+        switch (segment_sums_depth((int64_t)grid.x * grid.y, cols)) {
+            case 4 * kSegmentDepth:
+                launch_segment_sums_depth<4 * kSegmentDepth, PARTS, RUN>(grid, block, vec4, x, total_rows, offsets,
+                                                                          units, parts, cols, dst, tail_counts, order,
+                                                                          stream);
+                break;
+            case 2 * kSegmentDepth:
+                launch_segment_sums_depth<2 * kSegmentDepth, PARTS, RUN>(grid, block, vec4, x, total_rows, offsets,
+                                                                          units, parts, cols, dst, tail_counts, order,
+                                                                          stream);
+                break;
+            default:
+                launch_segment_sums_depth<kSegmentDepth, PARTS, RUN>(grid, block, vec4, x, total_rows, offsets, units,
+                                                                      parts, cols, dst, tail_counts, order, stream);
+                break;
+        }
     }
 }
 
@@ -347,17 +379,23 @@ hipError_t launch_segment_sums(const loom_launch_config &cfg, const float *x, in
     float *partial = static_cast<float *>(workspace);
     const bool vec4 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                       (reinterpret_cast<uintptr_t>(partial) % 16 == 0) && (cols % 4 == 0);
-    launch_segment_units<true>(grid, block, vec4, x, total_rows, offsets, segments * parts, parts, cols, partial,
-                               tail_counts, nullptr, stream);
+    const int runs = segment_sums_runs(segments, cols, total_rows);
+    if (runs > 0)
+        launch_segment_units<true, kSegmentRunWaves>(grid, block, vec4, x, total_rows, offsets, segments * runs,
+                                                     parts, cols, partial, tail_counts, nullptr, stream);
+    else
+        launch_segment_units<true>(grid, block, vec4, x, total_rows, offsets, segments * parts, parts, cols,
+                                   partial, tail_counts, nullptr, stream);
     if (hipError_t e = hipGetLastError()) return e;
+    const int partials = runs > 0 ? runs : parts;
     const dim3 cgrid((unsigned)grid_stride_groups(segments, kWave * kSegmentCombineWaves), cfg.workgroups[1]);
     const dim3 cblock(kWave * kSegmentCombineWaves);
     if (vec4 && reinterpret_cast<uintptr_t>(out) % 16 == 0)
-        segment_sums_combine_kernel<4, kSegmentCombineDepth><<<cgrid, cblock, 0, stream>>>(partial, segments, parts,
-                                                                                          cols, out);
+        segment_sums_combine_kernel<4, kSegmentCombineDepth><<<cgrid, cblock, 0, stream>>>(partial, segments,
+                                                                                          partials, cols, out);
     else
-        segment_sums_combine_kernel<1, kSegmentCombineDepth><<<cgrid, cblock, 0, stream>>>(partial, segments, parts,
-                                                                                          cols, out);
+        segment_sums_combine_kernel<1, kSegmentCombineDepth><<<cgrid, cblock, 0, stream>>>(partial, segments,
+                                                                                          partials, cols, out);
     return hipGetLastError();
 }
 

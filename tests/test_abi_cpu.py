@@ -106,14 +106,25 @@ def test_launch_config_tiles(loom):
     assert loom.launch_config_invoke(seg, [5, 0, 10**9])["workgroups"] == (5, 1, 1)  # still writes the tail counts
     # few long segments (fewer than 192 segment waves, at least 1024 rows on
     # average): P parts per segment, parts of at least 512 rows on average,
-    # P * waves <= 4096
-    for segments, cols, total, parts in ((4, 256, 4 * 2**20, 1024), (3, 256, 120000, 78), (3, 1000, 120000, 78),
-                                         (47, 1000, 10**7, 21), (48, 1000, 10**7, 1), (191, 256, 10**8, 21),
-                                         (192, 256, 10**8, 1), (10, 256, 10239, 1), (10, 256, 10240, 2),
-                                         (2, 2**20, 10**6, 1), (1, 4096, 2**20, 256)):
+    # P * waves <= 4096.  Rows of at most 512 columns split into 16 parts or
+    # more take P a multiple of 8 and run the parts in runs of 8, an 8-wave
+    # workgroup per run (LDS: the run's 8 part sums of one 256-column block);
+    # otherwise a wave per part.
+    for segments, cols, total, parts, runs in (
+            (4, 256, 4 * 2**20, 1024, 128), (3, 256, 120000, 72, 9), (3, 1000, 120000, 78, 0),
+            (47, 1000, 10**7, 21, 0), (48, 1000, 10**7, 1, 0), (191, 256, 10**8, 16, 2), (192, 256, 10**8, 1, 0),
+            (10, 256, 10239, 1, 0), (10, 256, 10240, 2, 0), (2, 2**20, 10**6, 1, 0), (1, 4096, 2**20, 256, 0),
+            (1, 256, 15 * 512, 15, 0), (1, 256, 16 * 512, 16, 2), (1, 256, 31 * 512, 24, 3),
+            (1, 512, 2**21, 2048, 256), (2, 513, 2**21, 682, 0), (1, 1, 40 * 512, 40, 5), (5, 200, 6 * 512 * 5, 6, 0)):
         blocks = -(-cols // 256)
         cfg = loom.launch_config_invoke(seg, [segments, cols, total])
-        assert cfg["workgroups"] == (segments * parts, blocks, 1), (segments, cols, total)
+        if runs:
+            assert parts == 8 * runs
+            assert cfg["workgroups"] == (segments * runs, blocks, 1), (segments, cols, total)
+            assert cfg["workgroup_size"] == (512, 1, 1) and cfg["workgroup_storage_bytes"] == 8 * 1024
+        else:
+            assert cfg["workgroups"] == (segments * parts, blocks, 1), (segments, cols, total)
+            assert cfg["workgroup_size"] == (64, 1, 1) and cfg["workgroup_storage_bytes"] == 0
     i8 = loom.launch_config_lookup("i8_dequant_dot")
     # one vector, always a v_dot4 GEMV: rows of 6 to 8 whole 1 KiB records a
     # workgroup per row with a wave per 2 records (LDS: the wave totals) ...

@@ -256,8 +256,16 @@ SPLIT_CASES = [
 
 
 def _parts(loom, segments, cols, total):
+    # one wave per part, whether a part's wave has a workgroup to itself or
+    # sits in a run of parts
     cfg = loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"), [segments, cols, total])
-    return cfg["workgroups"][0] // segments
+    return cfg["workgroups"][0] * (cfg["workgroup_size"][0] // 64) // segments
+
+
+def _runs(loom, segments, cols, total):
+    # the parts go in runs, a multi-wave workgroup per run
+    cfg = loom.launch_config_invoke(loom.launch_config_lookup("segment_sums"), [segments, cols, total])
+    return cfg["workgroup_size"][0] > 64
 
 
 @pytest.mark.parametrize("lengths,cols", SPLIT_CASES)
@@ -386,6 +394,11 @@ BOUNDARY_CASES = [
     ("in_order", lambda: _alternating(4096, 256, 768), 64),                     # 512
     ("in_order", lambda: _alternating(4096, 256, 768), 31),                     # 2^26 - 2^21 floats
     ("in_order", lambda: _alternating(4096, 256, 768), 32),                     # 2^26
+    ("split", lambda: torch.full((1,), 15 * 512, dtype=torch.int64), 256),      # 15 parts: one partial per part
+    ("runs", lambda: torch.full((1,), 16 * 512, dtype=torch.int64), 256),       # 16 parts: 2 runs of 8
+    ("runs", lambda: torch.full((2,), 31 * 512, dtype=torch.int64), 512),       # 31 -> 24 parts, 512 columns
+    ("split", lambda: torch.full((2,), 31 * 512, dtype=torch.int64), 513),      # 513 columns: no runs
+    ("runs", lambda: torch.tensor([40 * 512 + 77, 9 * 512], dtype=torch.int64), 3),  # 32-bit path, ragged
 ]
 
 
@@ -396,14 +409,15 @@ def test_segment_sums_form_boundaries(loom, device, form, lengths, cols):
     off = synth.segment_offsets(L)
     total = int(off[-1])
     S = L.numel()
-    assert (_parts(loom, S, cols, total) > 1) == (form == "split")
+    assert (_parts(loom, S, cols, total) > 1) == (form != "in_order")
+    assert _runs(loom, S, cols, total) == (form == "runs")
     x = synth.segment_rows(synth.SEGMENTS.seed, 0, total, cols)
     dx, doff = x.to(device), off.to(device)
     out, tails = loom.segment_sums(dx, doff)
     g = _np(out)
     ref, rtails, d, a = oracle.segment_sums(x.numpy(), off.numpy())
     assert np.array_equal(_np(tails), rtails)
-    if form == "split":
+    if form != "in_order":
         assert_sum_close(g, ref, d, a, what=f"split boundary {S}x{cols}")
         again, _ = loom.segment_sums(dx, doff)
         assert np.array_equal(_np(again).view(np.uint32), g.view(np.uint32))

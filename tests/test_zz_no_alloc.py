@@ -37,7 +37,9 @@ def _call(lib, fn, x, off, cols):
 # (lengths, cols) of the two calls; the second is smaller than the first
 # (fewer rows, segments and columns)
 CALLS = {
-    "split": [([100000, 5, 60000], 256), ([30000, 20000], 100)],
+    # parts in runs of 8 (up to 512 columns), then a part per partial (wider
+    # rows), then runs again on a smaller input
+    "split": [([100000, 5, 60000], 256), ([40000, 7, 20000], 1000), ([30000, 20000], 100)],
     # 2 to 2^15 segments averaging >= 512 rows, >= 2^26 floats
     "longest_first": [([1300, 0, 37, 900] * 80, 512), ([9, 1500] * 95, 480)],
     "single": [([300, 0, 37, 900] * 100, 260), ([9, 400] * 150, 64)],
@@ -52,7 +54,8 @@ def test_noalloc_matches_segment_sums(loom, device, mode):
         L = torch.tensor(lengths, dtype=torch.int64)
         off = synth.segment_offsets(L)
         total = int(off[-1])
-        parts = loom.launch_config_invoke(seg, [len(lengths), cols, total])["workgroups"][0] // len(lengths)
+        cfg = loom.launch_config_invoke(seg, [len(lengths), cols, total])
+        parts = cfg["workgroups"][0] * (cfg["workgroup_size"][0] // 64) // len(lengths)  # a wave per part
         assert (parts > 1) == (mode == "split"), parts
         if mode != "split":
             ordered = total // len(lengths) >= 512 and total * cols >= 2 ** 26
