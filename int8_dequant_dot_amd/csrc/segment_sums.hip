@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kWave * RUN) void segment_sums_kernel(const float *
             const int lane_col = active ? lane * VEC : -cb;  // inactive lanes read the row's first columns
             V acc = V(0.0f);
             // the straight drain for runs: no copies of the ring at the register
-            // budget of a 16-wave workgroup
+            // budget of a run's workgroup
             pipelined<DEPTH, V, (RUN > 1)>(
                 count,
                 [&]() {
@@ -329,8 +329,9 @@ static void launch_segment_sums_depth(dim3 grid, dim3 block, bool vec4, const fl
 }
 
 // The read-ahead depth follows the launch's wave count and the row width; a
-// run's 16 waves keep the base depth (a deeper ring of 4-wide records does not
-// fit their register budget).
+// run's waves keep the base depth (a split launch big enough for the depth to
+// matter has thousands of waves, where the base depth is the one chosen
+// anyway).
 template <bool PARTS, int RUN = 1>
 static void launch_segment_units(dim3 grid, dim3 block, bool vec4, const float *x, int64_t total_rows,
                                  const int64_t *offsets, int64_t units, int parts, int cols, float *dst,
