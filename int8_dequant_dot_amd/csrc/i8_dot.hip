@@ -148,6 +148,10 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
     int lcol = 0;
     // consumer state
     int acc = 0, crec = 0, crow = 0, mine = 0;
+    // the epilogue's scales, read before the stream (after it, their latency
+    // would land on the wave's critical path)
+    const float ws = w_scale[row0 + min(lane, nrows - 1)];
+    const float xs = x_scale ? x_scale[0] : 1.0f;
 
     // a row of 8192 bytes is 8 records, most of them in the drain: the straight
     // drain measured about 3 % faster here
@@ -180,8 +184,8 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
     if (lane < nrows) {
         const int row = row0 + lane;
         float y = (float)mine;
-        y = y * w_scale[row];
-        if (x_scale) y = y * x_scale[0];
+        y = y * ws;
+        if (x_scale) y = y * xs;
         out[row] = y;
         if (acc_out) acc_out[row] = mine;
     }
@@ -212,8 +216,10 @@ __global__ __launch_bounds__(kWave * kGemvWideMaxWaves) void i8_gemv_wide_kernel
     const int first = min(records, wave * per);
     const int n = min(records, first + per) - first;
     __shared__ int part[kGemvWideMaxWaves];
+    const float xs = x_scale ? x_scale[0] : 1.0f;
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
         const int32_t *wrow = w + row * kw;
+        const float ws = w_scale[row];  // read before the row's stream, used after it
         int lcol = first * kBlockWords;
         int acc = 0;
         pipelined<DEPTH, GemvRecord>(
@@ -234,8 +240,8 @@ __global__ __launch_bounds__(kWave * kGemvWideMaxWaves) void i8_gemv_wide_kernel
             int sum = 0;
             for (int v = 0; v < waves; ++v) sum += part[v];
             float y = (float)sum;
-            y = y * w_scale[row];
-            if (x_scale) y = y * x_scale[0];
+            y = y * ws;
+            if (x_scale) y = y * xs;
             out[row] = y;
             if (acc_out) acc_out[row] = sum;
         }
@@ -279,6 +285,9 @@ __global__ __launch_bounds__(kWave) void i8_gemv_grouped_kernel(const int32_t *_
     // producer: group lg, piece lp; consumer: group cg, piece cp
     int lg = 0, lp = 0, cg = 0, cp = 0, acc = 0, mine = 0;
     const int32_t *lrow = first + (int64_t)(sub < left ? sub : 0) * kw;
+    // the epilogue's scales, read before the stream
+    const float ws = w_scale[row0 + min(lane, left - 1)];
+    const float xs = x_scale ? x_scale[0] : 1.0f;
     pipelined<DEPTH, GemvRecord>(
         groups * pieces,
         [&]() {
@@ -310,8 +319,8 @@ __global__ __launch_bounds__(kWave) void i8_gemv_grouped_kernel(const int32_t *_
     if (lane < left) {
         const int row = row0 + lane;
         float y = (float)mine;
-        y = y * w_scale[row];
-        if (x_scale) y = y * x_scale[0];
+        y = y * ws;
+        if (x_scale) y = y * xs;
         out[row] = y;
         if (acc_out) acc_out[row] = mine;
     }
@@ -348,6 +357,9 @@ __global__ __launch_bounds__(kWave) void i8_gemv_narrow_kernel(const int32_t *__
     const int4v xv = nrec > 0 ? load_words<false, VEC16, false, true>(x, c, kw) : int4v{0, 0, 0, 0};
     const int32_t *first = w + (int64_t)row0 * kw;
     int lrec = 0, crec = 0, mine = 0;
+    // the epilogue's scales, read before the stream
+    const float ws = w_scale[row0 + min(lane, left - 1)];
+    const float xs = x_scale ? x_scale[0] : 1.0f;
     pipelined<DEPTH, int4v>(
         nrec,
         [&]() {
@@ -367,8 +379,8 @@ __global__ __launch_bounds__(kWave) void i8_gemv_narrow_kernel(const int32_t *__
     if (lane < left) {
         const int row = row0 + lane;
         float y = (float)mine;
-        y = y * w_scale[row];
-        if (x_scale) y = y * x_scale[0];
+        y = y * ws;
+        if (x_scale) y = y * xs;
         out[row] = y;
         if (acc_out) acc_out[row] = mine;
     }
@@ -443,6 +455,15 @@ __global__ __launch_bounds__(kWave * KS) void i8_mfma_kernel(const int32_t *__re
     int4v acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = int4v{0, 0, 0, 0};
+    // The epilogue's scales (wave 0 writes the tile), read before the stream:
+    // read after it, their latency lands on every workgroup's critical path.
+    float ws_pre[4] = {}, xs_pre[NT] = {};
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws_pre[i] = w_scale[row_clamped(row0, 4 * g + i, rows)];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) xs_pre[t] = x_scale ? x_scale[min(t * 16 + m, batch - 1)] : 1.0f;
+    }
 
     int lrec = first;
     pipelined<DEPTH, MfmaRecord<S, NT>>(
@@ -511,14 +532,14 @@ __global__ __launch_bounds__(kWave * KS) void i8_mfma_kernel(const int32_t *__re
     for (int t = 0; t < NT; ++t) {
         const int n = t * 16 + m;
         if (n >= batch) continue;
-        const float xs = x_scale ? x_scale[n] : 1.0f;
+        const float xs = xs_pre[t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (4 * g + i < rows - row0) {
                 const int row = row0 + 4 * g + i;
                 const int a = acc[t][i];
                 float y = (float)a;
-                y = y * w_scale[row];
+                y = y * ws_pre[i];
                 if (x_scale) y = y * xs;
                 out[(int64_t)row * batch + n] = y;
                 if (acc_out) acc_out[(int64_t)row * batch + n] = a;
@@ -570,8 +591,16 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
         bfrag[s] = m < batch ? v : int4v{0, 0, 0, 0};
     }
 
+    // The epilogue's scales: thread (r, n) < 256 scales output (r, n) of every
+    // tile.  x_scale is read once; w_scale[row r of tile t] is read with the
+    // tile's rows, before them, so it has arrived when the rows have (read in
+    // the epilogue, it would wait for the next tile's loads as well).
+    const int er = (threadIdx.x >> 4) & 15, en = threadIdx.x & 15;
+    const float xs = x_scale ? x_scale[min(en, batch - 1)] : 1.0f;
+    float ws_next = 0.0f, ws = 0.0f;
     int4v rowbuf[CHUNKS];
     auto load_row = [&](int t) {
+        ws_next = w_scale[row_clamped(t * kMfmaTileRows, er, rows)];
         // rows past the end load the last row; their outputs are never stored
         const int32_t *src = w + (int64_t)row_clamped(t * kMfmaTileRows, wave, rows) * kw;
 #pragma unroll
@@ -586,6 +615,7 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
             const int c = j * kWave + lane;
             tile[wave * kUnits + (c ^ wave)] = rowbuf[j];
         }
+        ws = ws_next;
         if (t + (int)gridDim.x < ntiles) load_row(t + gridDim.x);
         __syncthreads();
         int4v acc = int4v{0, 0, 0, 0};
@@ -599,14 +629,14 @@ __global__ __launch_bounds__(kWave * kI8RowsWaves) void i8_mfma_rows_kernel(
         __syncthreads();
         if (threadIdx.x < kMfmaTileRows * 16) {
             // output (r, n) of the tile sits in lane 16 (r / 4) + n, slot r % 4, of every partial
-            const int r = threadIdx.x >> 4, n = threadIdx.x & 15;
+            const int r = er, n = en;
             int sum = 0;
             for (int v = 0; v < kI8RowsWaves; ++v) sum += partial[v][r & 3][(r >> 2) * 16 + n];
             if (n < batch && r < rows - t * kMfmaTileRows) {
                 const int row = t * kMfmaTileRows + r;
                 float y = (float)sum;
-                y = y * w_scale[row];
-                if (x_scale) y = y * x_scale[n];
+                y = y * ws;
+                if (x_scale) y = y * xs;
                 out[(int64_t)row * batch + n] = y;
                 if (acc_out) acc_out[(int64_t)row * batch + n] = sum;
             }
