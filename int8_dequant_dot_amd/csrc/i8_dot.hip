@@ -43,14 +43,10 @@ namespace loom {
 // 1, 5 and 11 overall.
 #define LOOM_I8_COLS_STAGGER 5
 #endif
-#ifndef LOOM_GEMV_WIDE_DEPTH
-#define LOOM_GEMV_WIDE_DEPTH 3   // a wave's two 1 KiB records at k = 8192 issued at once
-#endif
 #ifndef LOOM_GEMV_NARROW_DEPTH
 #define LOOM_GEMV_NARROW_DEPTH 6
 #endif
 constexpr int kGemvDepth = LOOM_GEMV_DEPTH;
-constexpr int kGemvWideDepth = LOOM_GEMV_WIDE_DEPTH;
 constexpr int kGemvNarrowDepth = LOOM_GEMV_NARROW_DEPTH;
 constexpr int kMfmaDepth = LOOM_MFMA_DEPTH;
 constexpr int kMfmaSteps = LOOM_MFMA_STEPS;
@@ -192,59 +188,51 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
 }
 
 // ----------------------------------------------------------------------------
-// One vector, long rows of whole 1 KiB records (gemv_form): one workgroup per
-// row, of gemv_wide_waves(k) waves -- about LOOM_GEMV_WIDE_RECORDS records
-// each, at most kGemvWideMaxWaves.  Wave w streams a contiguous share of the
-// row's records, folds them with v_dot4 into per-lane int32 partials,
-// reduces them across the wave, and the wave totals are added in wave order
-// (exact).  Every wave of the launch reads a short contiguous stretch of one
-// row with all of its loads issued almost at once, which is what the HBM
-// stream favours.  Past the work-item limit of a grid, each workgroup takes
-// every grid.x-th row.
+// One vector, rows of 6 to 8 whole 1 KiB records (gemv_form): one workgroup per
+// row of WAVES = gemv_wide_waves(k) waves.  Wave w reads records 2w and 2w+1
+// of the row (the last wave only 2w when the count is odd), all of its loads
+// issued at once, weights first; folds them with v_dot4 into per-lane int32
+// partials, reduces them across the wave, and the wave totals are added in
+// wave order (exact).  Every wave of the launch reads one contiguous 2 KiB
+// stretch of a row, which is what the HBM stream favours, and the code before
+// the first load is kept short: a wave lives about one memory round trip, so
+// its start-up latency is a visible share of it.  STRIDE: the grid stopped at
+// the work-item limit and each workgroup takes every grid.x-th row.
 // ----------------------------------------------------------------------------
-template <bool FULL, bool VEC16, int DEPTH>
-__global__ __launch_bounds__(kWave * kGemvWideMaxWaves) void i8_gemv_wide_kernel(
+template <bool VEC16, int WAVES, bool STRIDE>
+__global__ __launch_bounds__(kWave * WAVES) void i8_gemv_wide_kernel(
     const int32_t *__restrict__ w, const float *__restrict__ w_scale, const int32_t *__restrict__ x,
     const float *__restrict__ x_scale, int rows, int kw, float *__restrict__ out, int32_t *__restrict__ acc_out) {
-    static_assert(FULL, "rows of whole 1 KiB records");
     constexpr int kBlockWords = kWave * 4;
     const int lane = lane_id();
-    const int waves = blockDim.x / kWave;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    const int records = kw / kBlockWords + (kw % kBlockWords != 0);
-    const int per = (records + waves - 1) / waves;
-    const int first = min(records, wave * per);
-    const int n = min(records, first + per) - first;
-    __shared__ int part[kGemvWideMaxWaves];
-    const float xs = x_scale ? x_scale[0] : 1.0f;
+    const bool two = (2 * wave + 2) * kBlockWords <= kw;  // wave-uniform
+    const int c = 2 * wave * kBlockWords + lane * 4;
+    __shared__ int part[WAVES];
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
         const int32_t *wrow = w + row * kw;
-        const float ws = w_scale[row];  // read before the row's stream, used after it
-        int lcol = first * kBlockWords;
-        int acc = 0;
-        pipelined<DEPTH, GemvRecord>(
-            n,
-            [&]() {
-                GemvRecord q;
-                const int c = lcol + lane * 4;
-                q.xv = load_words<FULL, VEC16, false, true>(x, c, kw);
-                q.wv = load_words<FULL, VEC16, true, true>(wrow, c, kw);
-                lcol += kBlockWords;
-                return q;
-            },
-            [&](const GemvRecord &q) { acc = dot16(q.wv, q.xv, acc); });
-        const int total = wave_sum(acc);
+        const int4v w0 = load_words<true, VEC16, true>(wrow, c, kw);
+        int4v w1 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+        if (two) w1 = load_words<true, VEC16, true>(wrow, c + kBlockWords, kw);
+        const int4v x0 = load_words<true, VEC16, false>(x, c, kw);
+        if (two) x1 = load_words<true, VEC16, false>(x, c + kBlockWords, kw);
+        // the epilogue's scales, read while the stretch streams in
+        const float ws = w_scale[row];
+        const float xs = x_scale ? x_scale[0] : 1.0f;
+        const int total = wave_sum(dot16(w1, x1, dot16(w0, x0, 0)));
         if (lane == 0) part[wave] = total;
         __syncthreads();
         if (threadIdx.x == 0) {
-            int sum = 0;
-            for (int v = 0; v < waves; ++v) sum += part[v];
+            int sum = part[0];
+#pragma unroll
+            for (int v = 1; v < WAVES; ++v) sum += part[v];
             float y = (float)sum;
             y = y * ws;
             if (x_scale) y = y * xs;
             out[row] = y;
             if (acc_out) acc_out[row] = sum;
         }
+        if (!STRIDE) break;
         if (row + gridDim.x < rows) __syncthreads();  // part[] is rewritten for the next row
     }
 }
@@ -838,6 +826,31 @@ static void launch_gemv_narrow(dim3 grid, dim3 block, hipStream_t stream, const 
     }
 }
 
+template <int WAVES>
+static void launch_gemv_wide_waves(dim3 grid, dim3 block, hipStream_t stream, bool vec16, bool stride,
+                                   const int32_t *w, const float *w_scale, const int32_t *x, const float *x_scale,
+                                   int rows, int kw, float *out, int32_t *acc) {
+#define LOOM_WIDE(V, S) i8_gemv_wide_kernel<V, WAVES, S><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, out, acc)
+    if (vec16) {
+        if (stride) LOOM_WIDE(true, true); else LOOM_WIDE(true, false);
+    } else {
+        if (stride) LOOM_WIDE(false, true); else LOOM_WIDE(false, false);
+    }
+#undef LOOM_WIDE
+}
+
+// The wave count is the one the launch geometry (gemv_wide_waves) gives the
+// workgroup; the row lengths gemv_form admits need 3 or 4.
+static bool launch_gemv_wide(dim3 grid, dim3 block, hipStream_t stream, bool vec16, bool stride, const int32_t *w,
+                             const float *w_scale, const int32_t *x, const float *x_scale, int rows, int kw,
+                             float *out, int32_t *acc) {
+    switch (block.x / kWave) {
+        case 3: launch_gemv_wide_waves<3>(grid, block, stream, vec16, stride, w, w_scale, x, x_scale, rows, kw, out, acc); return true;
+        case 4: launch_gemv_wide_waves<4>(grid, block, stream, vec16, stride, w, w_scale, x, x_scale, rows, kw, out, acc); return true;
+        default: return false;
+    }
+}
+
 hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w, const float *w_scale,
                                  const int32_t *x, const float *x_scale, int rows, int k_words, int batch,
                                  float *out, int32_t *acc, hipStream_t stream) {
@@ -883,12 +896,9 @@ hipError_t launch_i8_dequant_dot(const loom_launch_config &cfg, const int32_t *w
                 break;
             }
             case kGemvWide:
-                if (vec16)
-                    i8_gemv_wide_kernel<true, true, kGemvWideDepth><<<grid, block, 0, stream>>>(
-                        w, w_scale, x, x_scale, rows, k_words, out, acc);
-                else
-                    i8_gemv_wide_kernel<true, false, kGemvWideDepth><<<grid, block, 0, stream>>>(
-                        w, w_scale, x, x_scale, rows, k_words, out, acc);
+                if (!launch_gemv_wide(grid, block, stream, vec16, (int64_t)grid.x < rows, w, w_scale, x, x_scale,
+                                      rows, k_words, out, acc))
+                    return hipErrorInvalidConfiguration;
                 break;
             default: {
                 const int rpw = gemv_rows_per_wave(k_words);

@@ -219,10 +219,11 @@ constexpr int64_t segment_sums_workspace_bytes(int64_t segments, int64_t cols, i
 #ifndef LOOM_GEMV_WIDE_MAX_K
 #define LOOM_GEMV_WIDE_MAX_K 8192
 #endif
-#ifndef LOOM_GEMV_WIDE_RECORDS
-#define LOOM_GEMV_WIDE_RECORDS 2  // 1 KiB records per wave of the wide form
-#endif
-constexpr int kGemvWideMaxWaves = 16;
+// the wide form: two 1 KiB records per wave, instantiated for 3 and 4 waves
+constexpr int kGemvWideRecords = 2;
+constexpr int kGemvWideMaxWaves = 4;
+static_assert(LOOM_GEMV_WIDE_MIN_K > 4096 && LOOM_GEMV_WIDE_MAX_K <= 8192,
+              "wide GEMV rows of 5 to 8 records: 3 or 4 waves");
 enum GemvForm : int { kGemvNarrow = 0, kGemvRows = 1, kGemvWide = 2, kGemvGrouped = 3 };
 constexpr GemvForm gemv_form(int64_t k) {
 #ifdef LOOM_GEMV_FORCE_FORM
@@ -237,7 +238,7 @@ constexpr GemvForm gemv_form(int64_t k) {
 }
 constexpr int gemv_wide_waves(int64_t k) {
     const int64_t records = (k + 1023) / 1024;
-    const int64_t wv = (records + LOOM_GEMV_WIDE_RECORDS - 1) / LOOM_GEMV_WIDE_RECORDS;
+    const int64_t wv = (records + kGemvWideRecords - 1) / kGemvWideRecords;
     return wv < 1 ? 1 : wv > kGemvWideMaxWaves ? kGemvWideMaxWaves : (int)wv;
 }
 constexpr bool i8_use_gemv(int64_t k, int64_t batch) { return batch == 1 && k >= 0; }

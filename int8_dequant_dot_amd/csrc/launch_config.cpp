@@ -105,8 +105,9 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
             case kGemvRows: return set(c, ceil_div(w[0], gemv_rows_per_wave(w[1] / 4)), kSubgroupSize, 0);
             case kGemvGrouped: return set(c, ceil_div(w[0], gemv_group_rows_per_wave(w[1])), kSubgroupSize, 0);
             default: {  // LDS: the wave totals
-                const int64_t size = kSubgroupSize * gemv_wide_waves(w[1]);
-                return set(c, grid_stride_groups(w[0], size), (uint32_t)size, 4 * kGemvWideMaxWaves);
+                const int waves = gemv_wide_waves(w[1]);
+                const int64_t size = kSubgroupSize * waves;
+                return set(c, grid_stride_groups(w[0], size), (uint32_t)size, 4u * (uint32_t)waves);
             }
         }
     }

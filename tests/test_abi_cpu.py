@@ -131,7 +131,7 @@ def test_launch_config_tiles(loom):
     for k, waves in ((6144, 3), (7168, 4), (8192, 4)):
         cfg = loom.launch_config_invoke(i8, [100, k, 1])
         assert cfg["workgroups"] == (100, 1, 1) and cfg["workgroup_size"] == (64 * waves, 1, 1), k
-        assert cfg["workgroup_storage_bytes"] == 64, k
+        assert cfg["workgroup_storage_bytes"] == 4 * waves, k
     assert loom.launch_config_invoke(i8, [16384, 8192, 1])["workgroups"][0] == 16384
     # ... other rows of whole 1 KiB records, and rows of 12 KiB or more, a wave
     # per block of about 8 KiB of rows (at least one row) ...

@@ -534,7 +534,8 @@ def test_i8_dequant_dot(loom, device, rows, k, batch):
 
 @pytest.mark.parametrize("rows,k,batch", [(70, 4096, 8), (70, 4096, 16), (70, 4096, 33), (70, 4096, 1),
                                            (4111, 8192, 5), (90, 2048, 2), (70, 6144, 12),
-                                           (70, 8192, 1), (70, 5000, 1), (70, 1536, 1), (70, 1028, 1),
+                                           (70, 8192, 1), (70, 7168, 1), (70, 6144, 1), (70, 5000, 1),
+                                           (70, 1536, 1), (70, 1028, 1),
                                            (130, 100, 1), (130, 12, 1)])
 def test_i8_unaligned_operands(loom, device, rows, k, batch):
     # weights and vectors starting 4 bytes past a 16-byte boundary: the kernels
