@@ -196,20 +196,23 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
 // wave order (exact).  Every wave of the launch reads one contiguous 2 KiB
 // stretch of a row, which is what the HBM stream favours, and the code before
 // the first load is kept short: a wave lives about one memory round trip, so
-// its start-up latency is a visible share of it.  STRIDE: the grid stopped at
-// the work-item limit and each workgroup takes every grid.x-th row.
+// its start-up latency is a visible share of it.  EVEN: the record count is
+// even, so no wave tests for a missing second record.  STRIDE: the grid
+// stopped at the work-item limit and each workgroup takes every grid.x-th row;
+// otherwise workgroup b takes row b and reads no bound first.
 // ----------------------------------------------------------------------------
-template <bool VEC16, int WAVES, bool STRIDE>
+template <bool VEC16, int WAVES, bool EVEN, bool STRIDE>
 __global__ __launch_bounds__(kWave * WAVES) void i8_gemv_wide_kernel(
     const int32_t *__restrict__ w, const float *__restrict__ w_scale, const int32_t *__restrict__ x,
     const float *__restrict__ x_scale, int rows, int kw, float *__restrict__ out, int32_t *__restrict__ acc_out) {
     constexpr int kBlockWords = kWave * 4;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    const bool two = (2 * wave + 2) * kBlockWords <= kw;  // wave-uniform
+    // EVEN: every wave has two records; else the last has one (wave-uniform)
+    const bool two = EVEN || (2 * wave + 2) * kBlockWords <= kw;
     const int c = 2 * wave * kBlockWords + lane * 4;
     __shared__ int part[WAVES];
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    auto one_row = [&](int64_t row) {
         const int32_t *wrow = w + row * kw;
         const int4v w0 = load_words<true, VEC16, true>(wrow, c, kw);
         int4v w1 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
@@ -232,8 +235,14 @@ __global__ __launch_bounds__(kWave * WAVES) void i8_gemv_wide_kernel(
             out[row] = y;
             if (acc_out) acc_out[row] = sum;
         }
-        if (!STRIDE) break;
-        if (row + gridDim.x < rows) __syncthreads();  // part[] is rewritten for the next row
+    };
+    if constexpr (!STRIDE) {
+        one_row(blockIdx.x);  // the grid has one workgroup per row
+    } else {
+        for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+            one_row(row);
+            __syncthreads();  // part[] is rewritten for the next row
+        }
     }
 }
 
@@ -830,12 +839,14 @@ template <int WAVES>
 static void launch_gemv_wide_waves(dim3 grid, dim3 block, hipStream_t stream, bool vec16, bool stride,
                                    const int32_t *w, const float *w_scale, const int32_t *x, const float *x_scale,
                                    int rows, int kw, float *out, int32_t *acc) {
-#define LOOM_WIDE(V, S) i8_gemv_wide_kernel<V, WAVES, S><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, out, acc)
-    if (vec16) {
-        if (stride) LOOM_WIDE(true, true); else LOOM_WIDE(true, false);
-    } else {
-        if (stride) LOOM_WIDE(false, true); else LOOM_WIDE(false, false);
-    }
+#define LOOM_WIDE(V, E, S) \
+    i8_gemv_wide_kernel<V, WAVES, E, S><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, out, acc)
+    const bool even = kw % (2 * kWave * 4) == 0;
+    if (vec16 && even && !stride) LOOM_WIDE(true, true, false);
+    else if (vec16 && !stride) LOOM_WIDE(true, false, false);
+    else if (!stride) LOOM_WIDE(false, false, false);
+    else if (vec16) LOOM_WIDE(true, false, true);
+    else LOOM_WIDE(false, false, true);
 #undef LOOM_WIDE
 }
 
