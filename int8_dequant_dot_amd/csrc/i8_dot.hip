@@ -24,6 +24,9 @@ namespace loom {
 #ifndef LOOM_MFMA_DEPTH
 #define LOOM_MFMA_DEPTH 3        // two 4 KiB records in flight per wave
 #endif
+#ifndef LOOM_MFMA_SEG_DEPTH
+#define LOOM_MFMA_SEG_DEPTH 3    // two 4 KiB records in flight per wave, 2-8 vectors
+#endif
 #ifndef LOOM_MFMA_STREAM
 // Non-temporal weight loads.  With LDS staging every load instruction reads
 // whole 128 B lines; without it (fragments straight from memory, half a line
@@ -49,6 +52,7 @@ namespace loom {
 constexpr int kGemvDepth = LOOM_GEMV_DEPTH;
 constexpr int kGemvNarrowDepth = LOOM_GEMV_NARROW_DEPTH;
 constexpr int kMfmaDepth = LOOM_MFMA_DEPTH;
+constexpr int kMfmaSegDepth = LOOM_MFMA_SEG_DEPTH;
 constexpr int kMfmaSteps = LOOM_MFMA_STEPS;
 constexpr int kI8ColsDepth = LOOM_I8_COLS_DEPTH;
 
@@ -547,6 +551,134 @@ __global__ __launch_bounds__(kWave * KS) void i8_mfma_kernel(const int32_t *__re
 
 
 // ----------------------------------------------------------------------------
+// Two to eight vectors: the segment-paired matrix-core kernel, with no LDS
+// staging.  One workgroup owns a 16-row tile; its KS waves (mfma_ksplit) each
+// take a contiguous share of k in records of 16 rows x 256 bytes, and their
+// int32 partials are added in wave order at the end (exact).  A k step's A
+// operand is 16 rows x 64 bytes; here its 16 rows are 4 weight rows x 4
+// segments of 64 bytes (A row m: weight row 4i + (m >> 2), bytes 64 (m & 3) ..
+// of the record's 256), and the B operand's 16 columns are 4 vectors x the
+// same 4 segments (column n: vector 4 vg + (n >> 2), segment n & 3).  Lane l
+// (m = l & 15, g = l >> 4) holds bytes 64 (m & 3) + 16 g .. + 15 of both, so
+// one load instruction reads 4 weight rows x 256 contiguous bytes straight
+// into the A layout.  D[m][n] adds segment (m & 3) of a row times segment
+// (n & 3) of a vector; only equal segments are wanted.  Lane l holds
+// D[4 (l >> 4) + e][l & 15], whose wanted entry is e = l & 3 (row 4i + (l >> 4),
+// vector 4 vg + ((l & 15) >> 2)), and the 4 lanes of a quad hold the 4
+// segments of one (row, vector) pair, added by two DPP steps after the
+// stream.  The matrix cores do 4 times the useful products, a few percent of
+// their peak here; in exchange no record passes through LDS.  VG: vector
+// groups of 4 (1 up to 4 vectors, 2 up to 8).
+// ----------------------------------------------------------------------------
+template <int VG>
+struct SegRecord {
+    int4v a[4];
+    int4v b[VG];
+};
+
+template <bool FULL, bool VEC16, int DEPTH, int VG, int KS>
+__global__ __launch_bounds__(kWave * KS) void i8_mfma_seg_kernel(const int32_t *__restrict__ w,
+                                                                 const float *__restrict__ w_scale,
+                                                                 const int32_t *__restrict__ x,
+                                                                 const float *__restrict__ x_scale, int rows, int kw,
+                                                                 int batch, float *__restrict__ out,
+                                                                 int32_t *__restrict__ acc_out) {
+    constexpr int kRecordWords = 64;       // 256 bytes of a row per record
+    constexpr int kOuts = 16 * 4 * VG;     // the tile's outputs: 16 rows x 4 VG vector slots
+    constexpr int kPer = (kOuts + kWave * KS - 1) / (kWave * KS);  // outputs per thread
+    const int lane = lane_id();
+    const int m = lane & 15, g = lane >> 4;
+    const int row0 = blockIdx.x * kMfmaTileRows;
+    const int loff = (m & 3) * 16 + g * 4;  // words: segment m & 3, 16-byte group g
+    const int32_t *wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = w + (int64_t)row_clamped(row0, 4 * i + (m >> 2), rows) * kw;
+    const int32_t *xrow[VG];
+    bool xlive[VG];
+#pragma unroll
+    for (int vg = 0; vg < VG; ++vg) {
+        const int v = 4 * vg + (m >> 2);
+        xlive[vg] = v < batch;
+        xrow[vg] = x + (int64_t)min(v, batch - 1) * kw;
+    }
+    // the same in every lane: keeps the wave's k share and loop count scalar
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int all_records = kw / kRecordWords + (kw % kRecordWords != 0);
+    const int per_wave = (all_records + KS - 1) / KS;
+    const int first = min(all_records, wave * per_wave);
+    const int records = min(all_records, first + per_wave) - first;
+
+    // The epilogue's scales, read before the stream: read after it, their
+    // latency lands on every workgroup's critical path.
+    float ws_pre[kPer], xs_pre[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int o = (int)threadIdx.x + j * kWave * KS;
+        const int r = min(o / (4 * VG), 15), v = o % (4 * VG);
+        ws_pre[j] = w_scale[row_clamped(row0, r, rows)];
+        xs_pre[j] = x_scale ? x_scale[min(v, batch - 1)] : 1.0f;
+    }
+
+    int4v acc[4][VG];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int vg = 0; vg < VG; ++vg) acc[i][vg] = int4v{0, 0, 0, 0};
+    int lrec = first;
+    pipelined<DEPTH, SegRecord<VG>>(
+        records,
+        [&]() {
+            SegRecord<VG> q;
+            const int c = lrec * kRecordWords + loff;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q.a[i] = load_words<FULL, VEC16, LOOM_MFMA_STREAM != 0>(wrow[i], c, kw);
+#pragma unroll
+            for (int vg = 0; vg < VG; ++vg) q.b[vg] = load_words<FULL, VEC16, false>(xrow[vg], c, kw);
+            ++lrec;
+            return q;
+        },
+        [&](const SegRecord<VG> &q) {
+#pragma unroll
+            for (int vg = 0; vg < VG; ++vg) {
+                const int4v b = live_b(q.b[vg], xlive[vg]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][vg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(q.a[i], b, acc[i][vg], 0, 0, 0);
+            }
+        });
+
+    // each quad adds its pair's 4 segments; its first lane publishes the sum
+    __shared__ int part[KS][kOuts];
+    const int e = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int vg = 0; vg < VG; ++vg) {
+            const int4v d = acc[i][vg];
+            int t = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
+            t = t + dpp<kDppQuadSwap1>(t);
+            t = t + dpp<kDppQuadSwap2>(t);
+            if (e == 0) part[wave][(4 * i + g) * (4 * VG) + 4 * vg + (m >> 2)] = t;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int o = (int)threadIdx.x + j * kWave * KS;
+        if (o >= kOuts) break;
+        const int r = o / (4 * VG), v = o % (4 * VG);
+        if (v >= batch || r >= rows - row0) continue;
+        int sum = part[0][o];
+#pragma unroll
+        for (int q = 1; q < KS; ++q) sum += part[q][o];
+        float y = (float)sum;
+        y = y * ws_pre[j];
+        if (x_scale) y = y * xs_pre[j];
+        out[(int64_t)(row0 + r) * batch + v] = y;
+        if (acc_out) acc_out[(int64_t)(row0 + r) * batch + v] = sum;
+    }
+}
+
+// ----------------------------------------------------------------------------
 // Nine to sixteen vectors, rows of 4 to 8 KiB streamed whole (the choice of
 // kernel is i8_rows_chunks).  One workgroup of 16 waves
 // per CU walks 16-row tiles (tile t, t + gridDim.x, ...).  Wave w holds row w
@@ -806,6 +938,19 @@ static bool launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t
     if (batch > 16)
         return launch_mfma_cols<FULL, VEC16>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc);
     // the split is the one the launch geometry (mfma_ksplit) describes
+    if (batch <= kMfmaSegMaxBatch) {
+        switch (mfma_ksplit(4 * (int64_t)kw, rows) * 2 + (batch > 4 ? 1 : 0)) {
+#define LOOM_SEG_CASE(KS, VG)                                                                                 \
+    case KS * 2 + (VG - 1):                                                                                   \
+        i8_mfma_seg_kernel<FULL, VEC16, kMfmaSegDepth, VG, KS>                                                \
+            <<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, batch, out, acc);                  \
+        return true;
+            LOOM_SEG_CASE(1, 1) LOOM_SEG_CASE(1, 2) LOOM_SEG_CASE(2, 1) LOOM_SEG_CASE(2, 2)
+            LOOM_SEG_CASE(4, 1) LOOM_SEG_CASE(4, 2) LOOM_SEG_CASE(8, 1) LOOM_SEG_CASE(8, 2)
+#undef LOOM_SEG_CASE
+            default: return false;
+        }
+    }
     switch (mfma_ksplit(4 * (int64_t)kw, rows)) {
 #define LOOM_MFMA_CASE(KS)                                                                                    \
     case KS:                                                                                                  \

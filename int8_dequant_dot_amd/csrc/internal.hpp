@@ -287,6 +287,10 @@ constexpr int mfma_ksplit(int64_t k, int64_t rows) {
 #define LOOM_MFMA_STAGE 1     // weights reach the MFMA through a per-wave LDS tile
 #endif
 constexpr int kMfmaTileRows = 16;
+// Up to this many vectors the segment-paired kernel runs (no LDS staging;
+// LDS holds only its waves' partial sums: KS x 16 rows x 4 or 8 vector slots).
+constexpr int kMfmaSegMaxBatch = 8;
+constexpr uint32_t mfma_seg_lds_bytes(int ks, int64_t batch) { return (uint32_t)ks * 16u * (batch > 4 ? 8u : 4u) * 4u; }
 constexpr bool kMfmaStage = LOOM_MFMA_STAGE != 0;
 constexpr uint32_t kMfmaStageBytes = 16 * 256;  // per wave: 16 rows x 256 B
 // Outputs per lane of the packed-dot recurrence: kPackedDotWide, spaced one

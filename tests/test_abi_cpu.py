@@ -152,10 +152,10 @@ def test_launch_config_tiles(loom):
         assert cfg["workgroups"] == (-(-1000 // rows_per_wave), 1, 1) and cfg["workgroup_size"] == (64, 1, 1), k
     cfg = loom.launch_config_invoke(i8, [28672, 8192, 8])
     assert cfg["workgroups"][0] == 1792
-    # 4 waves split k per 16-row tile; LDS: 3 waves' int32 partial tiles (1 KiB
-    # each) + 4 per-wave 16x256 B weight staging tiles
+    # 4 waves split k per 16-row tile; LDS: each wave's partial sums of the
+    # tile's 16 rows x 8 vectors (the segment-paired kernel stages nothing)
     assert cfg["workgroup_size"] == (256, 1, 1)
-    assert cfg["workgroup_storage_bytes"] == 3 * 1024 + 4 * 4096
+    assert cfg["workgroup_storage_bytes"] == 4 * 16 * 8 * 4
     # more than 16 vectors, four column tiles: one wave per 16-vector
     # column tile, the 16-row tiles shared evenly by one or two workgroups per
     # CU (at most 8 tiles per wave); LDS: two record slots of 256 B per row
@@ -192,7 +192,10 @@ def test_launch_config_tiles(loom):
         cfg = loom.launch_config_invoke(i8, shape)
         assert cfg["workgroups"][0] == -(-shape[0] // 16), shape
         assert cfg["workgroup_size"] == (64 * ks, 1, 1), shape
-        assert cfg["workgroup_storage_bytes"] == (ks - 1) * 1024 + ks * 4096, shape
+        if shape[2] <= 8:  # segment-paired kernel: each wave's 16 rows x 4 or 8 vector slots of int32
+            assert cfg["workgroup_storage_bytes"] == ks * 16 * (8 if shape[2] > 4 else 4) * 4, shape
+        else:
+            assert cfg["workgroup_storage_bytes"] == (ks - 1) * 1024 + ks * 4096, shape
     t = loom.launch_config_lookup("row_sum_tiles")
     assert loom.launch_config_invoke(t, [63])["workgroups"] == (1, 1, 1)
     assert loom.launch_config_invoke(t, [63])["workgroup_size"] == (64, 1, 1)
@@ -471,7 +474,7 @@ def test_no_kernel_spills_to_scratch(loom, tmp_path):
     kernels = _kernel_metadata(loom.LIB_PATH, tmp_path)
     names = " ".join(n for n, _, _ in kernels)
     for kernel in ("row_sums_kernel", "row_sums_wide_kernel", "segment_sums_kernel", "i8_gemv_kernel",
-                   "i8_mfma_kernel", "i8_mfma_rows_kernel", "i8_mfma_cols_kernel", "packed_dot_kernel", "packed_dot_spaced_kernel", "sum_guarded_rows_kernel",
+                   "i8_mfma_kernel", "i8_mfma_seg_kernel", "i8_mfma_rows_kernel", "i8_mfma_cols_kernel", "packed_dot_kernel", "packed_dot_spaced_kernel", "sum_guarded_rows_kernel",
                    "routed_combine_kernel", "row_sum_tiles_kernel", "copy_f32_kernel"):
         assert kernel in names, kernel
     spilled = [(n, p) for n, p, _ in kernels if p != 0]
