@@ -25,7 +25,9 @@ namespace loom {
 #define LOOM_MFMA_DEPTH 3        // two 4 KiB records in flight per wave
 #endif
 #ifndef LOOM_MFMA_SEG_DEPTH
-#define LOOM_MFMA_SEG_DEPTH 3    // two 4 KiB records in flight per wave, 2-8 vectors
+// one 4 KiB record in flight per wave: 8 vectors at k = 8192 measured the same
+// as depths 3 and 4 (35.5 / 35.5 / 35.3 us), at k = 16384 39.2 against 42.1 / 42.2
+#define LOOM_MFMA_SEG_DEPTH 2
 #endif
 #ifndef LOOM_MFMA_STREAM
 // Non-temporal weight loads.  With LDS staging every load instruction reads
@@ -551,8 +553,8 @@ __global__ __launch_bounds__(kWave * KS) void i8_mfma_kernel(const int32_t *__re
 
 
 // ----------------------------------------------------------------------------
-// Two to eight vectors: the segment-paired matrix-core kernel, with no LDS
-// staging.  One workgroup owns a 16-row tile; its KS waves (mfma_ksplit) each
+// Six to eight vectors (two to eight when 8 waves split k; mfma_seg): the
+// segment-paired matrix-core kernel, with no LDS staging.  One workgroup owns a 16-row tile; its KS waves (mfma_ksplit) each
 // take a contiguous share of k in records of 16 rows x 256 bytes, and their
 // int32 partials are added in wave order at the end (exact).  A k step's A
 // operand is 16 rows x 64 bytes; here its 16 rows are 4 weight rows x 4
@@ -938,7 +940,7 @@ static bool launch_mfma(dim3 grid, dim3 block, hipStream_t stream, const int32_t
     if (batch > 16)
         return launch_mfma_cols<FULL, VEC16>(grid, block, stream, w, w_scale, x, x_scale, rows, kw, batch, out, acc);
     // the split is the one the launch geometry (mfma_ksplit) describes
-    if (batch <= kMfmaSegMaxBatch) {
+    if (mfma_seg(4 * (int64_t)kw, rows, batch)) {
         switch (mfma_ksplit(4 * (int64_t)kw, rows) * 2 + (batch > 4 ? 1 : 0)) {
 #define LOOM_SEG_CASE(KS, VG)                                                                                 \
     case KS * 2 + (VG - 1):                                                                                   \

@@ -287,9 +287,24 @@ constexpr int mfma_ksplit(int64_t k, int64_t rows) {
 #define LOOM_MFMA_STAGE 1     // weights reach the MFMA through a per-wave LDS tile
 #endif
 constexpr int kMfmaTileRows = 16;
-// Up to this many vectors the segment-paired kernel runs (no LDS staging;
-// LDS holds only its waves' partial sums: KS x 16 rows x 4 or 8 vector slots).
-constexpr int kMfmaSegMaxBatch = 8;
+// The segment-paired kernel (no LDS staging; LDS holds only its waves'
+// partial sums: KS x 16 rows x 4 or 8 vector slots) takes 6 to 8 vectors, and
+// 2 to 8 when 8 waves split k.  Measured against the LDS-staged tile kernel
+// over 224 MiB of weights (one MI355X, the same bits): 8 vectors at k = 8192
+// 35.5 against 36.0 us, at k = 16384 39.2 against 41.8; 2 to 5 vectors at
+// k = 16384 37.1-38.0 against 38.8-39.7; but 2 to 5 vectors at k = 2048 and
+// 8192 34.4-34.9 against 35.2-36.8 on the tile kernel.
+#ifndef LOOM_MFMA_SEG_MIN_BATCH
+#define LOOM_MFMA_SEG_MIN_BATCH 6
+#endif
+#ifndef LOOM_MFMA_SEG_MAX_BATCH
+#define LOOM_MFMA_SEG_MAX_BATCH 8
+#endif
+constexpr int kMfmaSegMaxBatch = LOOM_MFMA_SEG_MAX_BATCH;
+static_assert(kMfmaSegMaxBatch <= 8, "the segment-paired kernel has two vector groups of 4");
+constexpr bool mfma_seg(int64_t k, int64_t rows, int64_t batch) {
+    return batch <= kMfmaSegMaxBatch && (batch >= LOOM_MFMA_SEG_MIN_BATCH || mfma_ksplit(k, rows) == 8);
+}
 constexpr uint32_t mfma_seg_lds_bytes(int ks, int64_t batch) { return (uint32_t)ks * 16u * (batch > 4 ? 8u : 4u) * 4u; }
 constexpr bool kMfmaStage = LOOM_MFMA_STAGE != 0;
 constexpr uint32_t kMfmaStageBytes = 16 * 256;  // per wave: 16 rows x 256 B

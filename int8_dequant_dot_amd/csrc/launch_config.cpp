@@ -96,9 +96,9 @@ int geo_segment_sums(const int64_t *w, loom_launch_config *c) {
 // i8_cols_tile_rows rows with one wave per 16-vector column tile (LDS: two
 // record slots of 256 bytes per row); otherwise one workgroup per
 // 16-row matrix-core tile whose mfma_ksplit(k, rows) waves split k (the LDS
-// holds their partial sums: for 2 to 8 vectors, the segment-paired kernel's
-// 16 x 4 or 16 x 8 per wave; for 9 to 16, the partial accumulator tiles and
-// the weight staging tiles).
+// holds their partial sums: for the segment-paired kernel (mfma_seg), its
+// 16 x 4 or 16 x 8 per wave; otherwise the partial accumulator tiles and the
+// weight staging tiles).
 int geo_i8(const int64_t *w, loom_launch_config *c) {
     if (w[0] < 0 || w[1] < 0 || w[2] < 1) return LOOM_ERR_RANGE;
     if (i8_use_gemv(w[1], w[2])) {
@@ -122,7 +122,7 @@ int geo_i8(const int64_t *w, loom_launch_config *c) {
         return set(c, ceil_div(w[0], i8_cols_tile_rows(w[0])), kSubgroupSize * mfma_col_tiles(w[2]),
                    i8_cols_lds_bytes(w[0]));
     const int ks = mfma_ksplit(w[1], w[0]);
-    if (w[2] <= kMfmaSegMaxBatch)
+    if (mfma_seg(w[1], w[0], w[2]))
         return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * ks, mfma_seg_lds_bytes(ks, w[2]));
     return set(c, ceil_div(w[0], kMfmaTileRows), kSubgroupSize * ks,
                (ks - 1) * 4 * kSubgroupSize * 4 + (kMfmaStage ? ks * kMfmaStageBytes : 0));
