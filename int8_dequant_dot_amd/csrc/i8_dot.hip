@@ -391,7 +391,10 @@ __global__ __launch_bounds__(kWave) void i8_gemv_narrow_kernel(const int32_t *__
 
 // ----------------------------------------------------------------------------
 // Several vectors (batch >= 2): the shared activations make this a dense
-// int8 contraction, so it runs on the matrix cores.  One workgroup owns a
+// int8 contraction, so it runs on the matrix cores.  This LDS-staged tile
+// kernel takes the batches no other kernel below takes (2 to 5 vectors unless
+// 8 waves split k, and 9 to 16 where the row kernel does not apply; mfma_seg,
+// i8_rows_chunks).  One workgroup owns a
 // 16-row tile; its KS waves (1, 2, 4 or 8: about 2 KiB of every row per wave,
 // mfma_ksplit) each take a contiguous share of k (of the records), and their
 // int32 partial tiles are added in wave order at the end (exact).  Each k step is one v_mfma_i32_16x16x64_i8:
