@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kWave) void i8_gemv_narrow_kernel(const int32_t *__
 // ----------------------------------------------------------------------------
 // Several vectors (batch >= 2): the shared activations make this a dense
 // int8 contraction, so it runs on the matrix cores.  This LDS-staged tile
-// kernel takes the batches no other kernel below takes (2 to 5 vectors unless
+// kernel takes the batches no other kernel below takes (2 to 6 vectors unless
 // 8 waves split k, and 9 to 16 where the row kernel does not apply; mfma_seg,
 // i8_rows_chunks).  One workgroup owns a
 // 16-row tile; its KS waves (1, 2, 4 or 8: about 2 KiB of every row per wave,
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(kWave * KS) void i8_mfma_kernel(const int32_t *__re
 
 
 // ----------------------------------------------------------------------------
-// Six to eight vectors (two to eight when 8 waves split k; mfma_seg): the
+// Seven or eight vectors (two to eight when 8 waves split k; mfma_seg): the
 // segment-paired matrix-core kernel, with no LDS staging.  One workgroup owns a 16-row tile; its KS waves (mfma_ksplit) each
 // take a contiguous share of k in records of 16 rows x 256 bytes, and their
 // int32 partials are added in wave order at the end (exact).  A k step's A

@@ -288,14 +288,15 @@ constexpr int mfma_ksplit(int64_t k, int64_t rows) {
 #endif
 constexpr int kMfmaTileRows = 16;
 // The segment-paired kernel (no LDS staging; LDS holds only its waves'
-// partial sums: KS x 16 rows x 4 or 8 vector slots) takes 6 to 8 vectors, and
+// partial sums: KS x 16 rows x 4 or 8 vector slots) takes 7 or 8 vectors, and
 // 2 to 8 when 8 waves split k.  Measured against the LDS-staged tile kernel
 // over 224 MiB of weights (one MI355X, the same bits): 8 vectors at k = 8192
 // 35.5 against 36.0 us, at k = 16384 39.2 against 41.8; 2 to 5 vectors at
-// k = 16384 37.1-38.0 against 38.8-39.7; but 2 to 5 vectors at k = 2048 and
-// 8192 34.4-34.9 against 35.2-36.8 on the tile kernel.
+// k = 16384 37.1-38.0 against 38.8-39.7; 7 vectors at k = 4096 and 8192
+// 36.5 / 35.4 against 36.7 / 35.6; but 2 to 6 vectors at k = 2048 to 8192
+// 34.4-36.2 on the tile kernel against 34.9-37.7.
 #ifndef LOOM_MFMA_SEG_MIN_BATCH
-#define LOOM_MFMA_SEG_MIN_BATCH 6
+#define LOOM_MFMA_SEG_MIN_BATCH 7
 #endif
 #ifndef LOOM_MFMA_SEG_MAX_BATCH
 #define LOOM_MFMA_SEG_MAX_BATCH 8

@@ -505,11 +505,12 @@ I8_CASES = [
     # the tile kernel and the row kernel with a single row, partial last
     # tiles and thousands of tiles
     (1, 2048, 2), (4111, 8192, 5), (12345, 6144, 15), (40000, 2048, 2), (333, 4096, 3),
-    # 6-8 vectors, and 2-8 vectors when 8 waves split k: the segment-paired
+    # 7-8 vectors, and 2-8 vectors when 8 waves split k: the segment-paired
     # kernel (A operand = 4 rows x 4 k segments, no LDS staging); one and two
-    # vector groups, ragged tiles, partial last records, 1 to 8 waves per tile
-    (13, 8192, 6), (70, 1024, 6), (33, 256, 7), (8200, 16384, 8), (8193, 16384, 2), (8300, 16384, 4),
-    (8210, 16388, 5), (600, 16384, 6),
+    # vector groups, ragged tiles, partial last records, 1 to 8 waves per tile;
+    # 6 vectors on the tile kernel next to it
+    (13, 8192, 7), (70, 1024, 7), (33, 256, 7), (8200, 16384, 8), (8193, 16384, 2), (8300, 16384, 4),
+    (8210, 16388, 5), (600, 16384, 7), (13, 8192, 6), (8200, 16384, 6),
     # 9-16 vectors with k a multiple of 1024 from 4096 to 8192: the row-streaming
     # kernel (one workgroup per CU walking 16-row tiles; 8197 rows give 513
     # tiles, so workgroups take two or three tiles each)
