@@ -194,10 +194,12 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
 }
 
 // ----------------------------------------------------------------------------
-// One vector, rows of 6 to 8 whole 1 KiB records (gemv_form): one workgroup per
-// row of WAVES = gemv_wide_waves(k) waves.  Wave w reads records 2w and 2w+1
-// of the row (the last wave only 2w when the count is odd), all of its loads
-// issued at once, weights first; folds them with v_dot4 into per-lane int32
+// One vector, rows of 6 to 8 whole 1 KiB records, or of 3 to 12 KiB that are
+// not whole records (gemv_form): one workgroup per row of WAVES =
+// gemv_wide_waves(k) waves.  Wave w reads records 2w and 2w+1 of the row (the
+// last wave only 2w when a whole-record count is odd; FULL false: the row's
+// last record partly empty, its lanes past the row reading the row's first
+// word and adding zero), all of its loads issued at once, weights first; folds them with v_dot4 into per-lane int32
 // partials, reduces them across the wave, and the wave totals are added in
 // wave order (exact).  Every wave of the launch reads one contiguous 2 KiB
 // stretch of a row, which is what the HBM stream favours, and the code before
@@ -207,24 +209,25 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
 // stopped at the work-item limit and each workgroup takes every grid.x-th row;
 // otherwise workgroup b takes row b and reads no bound first.
 // ----------------------------------------------------------------------------
-template <bool VEC16, int WAVES, bool EVEN, bool STRIDE>
+template <bool FULL, bool VEC16, int WAVES, bool EVEN, bool STRIDE>
 __global__ __launch_bounds__(kWave * WAVES) void i8_gemv_wide_kernel(
     const int32_t *__restrict__ w, const float *__restrict__ w_scale, const int32_t *__restrict__ x,
     const float *__restrict__ x_scale, int rows, int kw, float *__restrict__ out, int32_t *__restrict__ acc_out) {
     constexpr int kBlockWords = kWave * 4;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    // EVEN: every wave has two records; else the last has one (wave-uniform)
-    const bool two = EVEN || (2 * wave + 2) * kBlockWords <= kw;
+    // EVEN: every wave has two records; else the last has one (wave-uniform).
+    // Rows that are not whole records read both with guards.
+    const bool two = !FULL || EVEN || (2 * wave + 2) * kBlockWords <= kw;
     const int c = 2 * wave * kBlockWords + lane * 4;
     __shared__ int part[WAVES];
     auto one_row = [&](int64_t row) {
         const int32_t *wrow = w + row * kw;
-        const int4v w0 = load_words<true, VEC16, true>(wrow, c, kw);
+        const int4v w0 = load_words<FULL, VEC16, true, true>(wrow, c, kw);
         int4v w1 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-        if (two) w1 = load_words<true, VEC16, true>(wrow, c + kBlockWords, kw);
-        const int4v x0 = load_words<true, VEC16, false>(x, c, kw);
-        if (two) x1 = load_words<true, VEC16, false>(x, c + kBlockWords, kw);
+        if (two) w1 = load_words<FULL, VEC16, true, true>(wrow, c + kBlockWords, kw);
+        const int4v x0 = load_words<FULL, VEC16, false, true>(x, c, kw);
+        if (two) x1 = load_words<FULL, VEC16, false, true>(x, c + kBlockWords, kw);
         // the epilogue's scales, read while the stretch streams in
         const float ws = w_scale[row];
         const float xs = x_scale ? x_scale[0] : 1.0f;
@@ -989,25 +992,34 @@ template <int WAVES>
 static void launch_gemv_wide_waves(dim3 grid, dim3 block, hipStream_t stream, bool vec16, bool stride,
                                    const int32_t *w, const float *w_scale, const int32_t *x, const float *x_scale,
                                    int rows, int kw, float *out, int32_t *acc) {
-#define LOOM_WIDE(V, E, S) \
-    i8_gemv_wide_kernel<V, WAVES, E, S><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, out, acc)
+#define LOOM_WIDE(F, V, E, S) \
+    i8_gemv_wide_kernel<F, V, WAVES, E, S><<<grid, block, 0, stream>>>(w, w_scale, x, x_scale, rows, kw, out, acc)
+    const bool full = kw % (kWave * 4) == 0;
     const bool even = kw % (2 * kWave * 4) == 0;
-    if (vec16 && even && !stride) LOOM_WIDE(true, true, false);
-    else if (vec16 && !stride) LOOM_WIDE(true, false, false);
-    else if (!stride) LOOM_WIDE(false, false, false);
-    else if (vec16) LOOM_WIDE(true, false, true);
-    else LOOM_WIDE(false, false, true);
+    if (!full) {
+        if (vec16 && !stride) LOOM_WIDE(false, true, false, false);
+        else if (!stride) LOOM_WIDE(false, false, false, false);
+        else if (vec16) LOOM_WIDE(false, true, false, true);
+        else LOOM_WIDE(false, false, false, true);
+    } else if (vec16 && even && !stride) LOOM_WIDE(true, true, true, false);
+    else if (vec16 && !stride) LOOM_WIDE(true, true, false, false);
+    else if (!stride) LOOM_WIDE(true, false, false, false);
+    else if (vec16) LOOM_WIDE(true, true, false, true);
+    else LOOM_WIDE(true, false, false, true);
 #undef LOOM_WIDE
 }
 
 // The wave count is the one the launch geometry (gemv_wide_waves) gives the
-// workgroup; the row lengths gemv_form admits need 3 or 4.
+// workgroup; the row lengths gemv_form admits need 2 to 6.
 static bool launch_gemv_wide(dim3 grid, dim3 block, hipStream_t stream, bool vec16, bool stride, const int32_t *w,
                              const float *w_scale, const int32_t *x, const float *x_scale, int rows, int kw,
                              float *out, int32_t *acc) {
     switch (block.x / kWave) {
+        case 2: launch_gemv_wide_waves<2>(grid, block, stream, vec16, stride, w, w_scale, x, x_scale, rows, kw, out, acc); return true;
         case 3: launch_gemv_wide_waves<3>(grid, block, stream, vec16, stride, w, w_scale, x, x_scale, rows, kw, out, acc); return true;
         case 4: launch_gemv_wide_waves<4>(grid, block, stream, vec16, stride, w, w_scale, x, x_scale, rows, kw, out, acc); return true;
+        case 5: launch_gemv_wide_waves<5>(grid, block, stream, vec16, stride, w, w_scale, x, x_scale, rows, kw, out, acc); return true;
+        case 6: launch_gemv_wide_waves<6>(grid, block, stream, vec16, stride, w, w_scale, x, x_scale, rows, kw, out, acc); return true;
         default: return false;
     }
 }

@@ -190,8 +190,11 @@ constexpr int64_t segment_sums_workspace_bytes(int64_t segments, int64_t cols, i
 //            a row partly filled when k is not a multiple of 1024: a small
 //            share of such long rows);
 //   wide     k a multiple of 1024 from LOOM_GEMV_WIDE_MIN_K to
-//            LOOM_GEMV_WIDE_MAX_K: a workgroup per row of gemv_wide_waves(k)
-//            waves.
+//            LOOM_GEMV_WIDE_MAX_K, and k a multiple of 16 (not of 1024)
+//            above LOOM_GEMV_WIDE_PARTIAL_MIN_K and below
+//            LOOM_GEMV_GROUPED_MAX_K: a workgroup per row of
+//            gemv_wide_waves(k) waves, each reading 2 KiB of the row (the
+//            row's last record partly empty).
 // Over 128 MiB of weights (one MI355X, back-to-back launches) each form was
 // kept where it measured fastest: rows of 768 to 8704 bytes that are not whole
 // 1 KiB records took 21.0-23.0 us grouped against 23.1-24.5 us in 1 KiB
@@ -199,7 +202,11 @@ constexpr int64_t segment_sums_workspace_bytes(int64_t segments, int64_t cols, i
 // record costs less than pairs of 512-byte pieces (k = 12800: 23.5 against
 // 23.9 us); a workgroup per row won only at 6-8 KiB rows (k = 6144:
 // 20.5 against 20.9 us; k = 4096: 22.2 against 20.7; k = 10240: 22.0 against
-// 21.1).
+// 21.1).  For rows that are not whole records, a workgroup per row with the
+// last record partly empty beat the grouped form from 3.25 to 11.5 KiB
+// (k = 3328 / 4608 / 7680 / 11008 / 11776: 22.2 / 21.6 / 21.1 / 22.0 /
+// 22.4 against 22.9 / 22.7 / 23.4 / 30.9 / 22.8 us; the grouped form gave a
+// 11008-byte row only 3048 waves of 4 rows each) and tied at 12800.
 // Several vectors run an int8 MFMA kernel: one 16-row matrix-core tile per
 // workgroup, whose KSPLIT waves split the k range and combine their int32
 // partials through LDS in wave order (exact).  Tuning builds may override the
@@ -219,11 +226,15 @@ constexpr int64_t segment_sums_workspace_bytes(int64_t segments, int64_t cols, i
 #ifndef LOOM_GEMV_WIDE_MAX_K
 #define LOOM_GEMV_WIDE_MAX_K 8192
 #endif
-// the wide form: two 1 KiB records per wave, instantiated for 3 and 4 waves
+#ifndef LOOM_GEMV_WIDE_PARTIAL_MIN_K
+#define LOOM_GEMV_WIDE_PARTIAL_MIN_K 3072
+#endif
+// the wide form: two 1 KiB records per wave, instantiated for 2 to 6 waves
 constexpr int kGemvWideRecords = 2;
-constexpr int kGemvWideMaxWaves = 4;
-static_assert(LOOM_GEMV_WIDE_MIN_K > 4096 && LOOM_GEMV_WIDE_MAX_K <= 8192,
-              "wide GEMV rows of 5 to 8 records: 3 or 4 waves");
+constexpr int kGemvWideMaxWaves = 6;
+static_assert(LOOM_GEMV_WIDE_MIN_K > 2048 && LOOM_GEMV_WIDE_MAX_K <= 12288 && LOOM_GEMV_WIDE_PARTIAL_MIN_K >= 2048 &&
+                  LOOM_GEMV_GROUPED_MAX_K <= 12288,
+              "wide GEMV rows of 3 to 12 records: 2 to 6 waves");
 enum GemvForm : int { kGemvNarrow = 0, kGemvRows = 1, kGemvWide = 2, kGemvGrouped = 3 };
 constexpr GemvForm gemv_form(int64_t k) {
 #ifdef LOOM_GEMV_FORCE_FORM
@@ -231,7 +242,9 @@ constexpr GemvForm gemv_form(int64_t k) {
         (LOOM_GEMV_FORCE_FORM == kGemvGrouped || k % 1024 == 0))
         return (GemvForm)LOOM_GEMV_FORCE_FORM;
 #endif
-    return k <= LOOM_GEMV_NARROW_MAX_K                                                  ? kGemvNarrow
+    return k <= LOOM_GEMV_NARROW_MAX_K ? kGemvNarrow
+           : k % 1024 != 0 && k % 16 == 0 && k > LOOM_GEMV_WIDE_PARTIAL_MIN_K && k < LOOM_GEMV_GROUPED_MAX_K
+               ? kGemvWide
            : k % 1024 != 0 && k < LOOM_GEMV_GROUPED_MAX_K                               ? kGemvGrouped
            : k % 1024 == 0 && k >= LOOM_GEMV_WIDE_MIN_K && k <= LOOM_GEMV_WIDE_MAX_K ? kGemvWide
                                                                                         : kGemvRows;

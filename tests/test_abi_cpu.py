@@ -126,9 +126,12 @@ def test_launch_config_tiles(loom):
             assert cfg["workgroups"] == (segments * parts, blocks, 1), (segments, cols, total)
             assert cfg["workgroup_size"] == (64, 1, 1) and cfg["workgroup_storage_bytes"] == 0
     i8 = loom.launch_config_lookup("i8_dequant_dot")
-    # one vector, always a v_dot4 GEMV: rows of 6 to 8 whole 1 KiB records a
-    # workgroup per row with a wave per 2 records (LDS: the wave totals) ...
-    for k, waves in ((6144, 3), (7168, 4), (8192, 4)):
+    # one vector, always a v_dot4 GEMV: rows of 6 to 8 whole 1 KiB records,
+    # and rows of more than 3 and less than 12 KiB that are a multiple of 16
+    # but not of 1024 bytes, a workgroup per row with a wave per 2 records (the
+    # last one partly empty; LDS: the wave totals) ...
+    for k, waves in ((6144, 3), (7168, 4), (8192, 4), (3088, 2), (3328, 2), (4608, 3), (8704, 5), (11008, 6),
+                     (12272, 6)):
         cfg = loom.launch_config_invoke(i8, [100, k, 1])
         assert cfg["workgroups"] == (100, 1, 1) and cfg["workgroup_size"] == (64 * waves, 1, 1), k
         assert cfg["workgroup_storage_bytes"] == 4 * waves, k
@@ -142,7 +145,7 @@ def test_launch_config_tiles(loom):
     # ... other rows longer than 512 bytes in groups of 2 rows x 512 B pieces (k
     # a multiple of 512) or 4 rows x 256 B, whole groups of about 8 KiB a wave ...
     for k, rows_per_wave in ((516, 12), (528, 12), (768, 8), (1028, 4), (1040, 4), (1280, 4), (1536, 4),
-                             (2560, 2), (4092, 4), (4100, 4), (8704, 2), (12284, 4)):
+                             (2560, 2), (3072 - 16, 4), (4092, 4), (4100, 4), (8708, 4), (12284, 4)):
         cfg = loom.launch_config_invoke(i8, [100, k, 1])
         assert cfg["workgroups"] == (-(-100 // rows_per_wave), 1, 1) and cfg["workgroup_size"] == (64, 1, 1), k
     # ... and rows of up to 512 bytes packed 64 / L to a record (16 L >= k),

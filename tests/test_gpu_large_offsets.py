@@ -186,11 +186,13 @@ def test_routed_combine_past_grid_limit(loom, device):
     assert np.array_equal(_bits(out), _bits(ref))
 
 
-@pytest.mark.parametrize("rows,k", [(20_000_000, 256), (3_000_000, 1536), (1_100_000, 4096), (2**24 + 100, 8192)])
+@pytest.mark.parametrize("rows,k", [(20_000_000, 256), (3_000_000, 1536), (1_100_000, 4096), (400_000, 11008),
+                                    (2**24 + 100, 8192)])
 def test_i8_gemv_forms_past_4gib(loom, device, rows, k):
     # one vector in each GEMV form over more than 4 GiB of weights: rows packed
     # several to a record, groups of rows per record, a wave per block of rows,
-    # and a workgroup per row (128 GiB) -- the last with more rows than a grid
+    # a workgroup per row whose last record is partly empty, and a workgroup
+    # per row of whole records (128 GiB) -- the last with more rows than a grid
     # of fewer than 2^32 work-items holds, so some workgroups take two rows
     if k == 8192:
         cfg = loom.launch_config_invoke(loom.launch_config_lookup("i8_dequant_dot"), [rows, k, 1])

@@ -496,6 +496,10 @@ I8_CASES = [
     # 9 KiB rows walk row by row), the grouped form up to 12284 bytes (12288
     # is whole records)
     (33, 6144, 1), (21, 7168, 1), (12, 5120, 1), (3, 9216, 1), (9, 12284, 1), (10, 12288, 1),
+    # rows of 3 to 12 KiB that are a multiple of 16 but not of 1024 bytes: a
+    # workgroup per row whose last record is partly empty (2 to 6 waves), next
+    # to the grouped form just below (3056) and the row form at 12288
+    (20, 3088, 1), (7, 3056, 1), (33, 4608, 1), (1, 5632, 1), (50, 8704, 1), (7, 11008, 1), (11, 12272, 1),
     (3, 64, 2), (15, 256, 3), (16, 260, 8), (17, 1000, 8), (100, 8192, 8), (33, 64, 16), (40, 512, 17),
     (20, 1024, 32), (18, 320, 33), (16, 4096, 64), (1, 4, 2), (31, 8, 5),
     # the tile kernel's k split: 1 wave per tile (k <= 2048, several records),
@@ -541,6 +545,7 @@ def test_i8_dequant_dot(loom, device, rows, k, batch):
 @pytest.mark.parametrize("rows,k,batch", [(70, 4096, 8), (70, 4096, 16), (70, 4096, 33), (70, 4096, 1),
                                            (4111, 8192, 5), (90, 2048, 2), (70, 6144, 12),
                                            (70, 8192, 1), (70, 7168, 1), (70, 6144, 1), (70, 5000, 1),
+                                           (70, 4608, 1), (70, 11008, 1),
                                            (70, 1536, 1), (70, 1028, 1),
                                            (130, 100, 1), (130, 12, 1)])
 def test_i8_unaligned_operands(loom, device, rows, k, batch):
