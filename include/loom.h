@@ -232,9 +232,10 @@ int loom_segment_sums_noalloc(const float *x, int64_t total_rows, const int64_t 
  *     out[r][b] = (f32(acc[r][b]) * w_scale[r]) * x_scale[b]                *
  * with each product rounded once to f32; when x_scale is NULL the second    *
  * product is skipped.  One vector runs a v_dot4 (int8x4) GEMV: rows of up  *
- * to 512 bytes packed several to a 1 KiB record, rows up to 4 KiB a wave    *
- * per block of rows, longer rows a workgroup per row.  Several vectors run  *
- * an int8 MFMA kernel.  The results are the same bits either way.           *
+ * to 512 bytes packed several to a 1 KiB record, most rows of 3 to 12 KiB   *
+ * a workgroup per row, other rows a wave per block of rows.  Several        *
+ * vectors run an int8 MFMA kernel.  The results are the same bits either    *
+ * way.                                                                      *
  *   w       : int32[rows][k/4] packed int8 weights, device, 4-byte aligned  *
  *   w_scale : f32[rows], device                                             *
  *   x       : int32[batch][k/4] packed int8 activations, device             *
