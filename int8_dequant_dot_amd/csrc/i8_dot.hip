@@ -199,9 +199,9 @@ __global__ __launch_bounds__(kWave) void i8_gemv_kernel(const int32_t *__restric
 // gemv_wide_waves(k) waves.  Wave w reads records 2w and 2w+1 of the row (the
 // last wave only 2w when a whole-record count is odd; FULL false: the row's
 // last record partly empty, its lanes past the row reading the row's first
-// word and adding zero), all of its loads issued at once, weights first; folds them with v_dot4 into per-lane int32
-// partials, reduces them across the wave, and the wave totals are added in
-// wave order (exact).  Every wave of the launch reads one contiguous 2 KiB
+// word and adding zero), all of its loads issued at once, weights first;
+// folds them with v_dot4 into per-lane int32 partials, reduces them across
+// the wave, and the wave totals are added in wave order (exact).  Every wave of the launch reads one contiguous 2 KiB
 // stretch of a row, which is what the HBM stream favours, and the code before
 // the first load is kept short: a wave lives about one memory round trip, so
 // its start-up latency is a visible share of it.  EVEN: the record count is
@@ -560,9 +560,10 @@ __global__ __launch_bounds__(kWave * KS) void i8_mfma_kernel(const int32_t *__re
 
 // ----------------------------------------------------------------------------
 // Seven or eight vectors (two to eight when 8 waves split k; mfma_seg): the
-// segment-paired matrix-core kernel, with no LDS staging.  One workgroup owns a 16-row tile; its KS waves (mfma_ksplit) each
-// take a contiguous share of k in records of 16 rows x 256 bytes, and their
-// int32 partials are added in wave order at the end (exact).  A k step's A
+// segment-paired matrix-core kernel, with no LDS staging.  One workgroup owns
+// a 16-row tile; its KS waves (mfma_ksplit) each take a contiguous share of k
+// in records of 16 rows x 256 bytes, and their int32 partials are added in
+// wave order at the end (exact).  A k step's A
 // operand is 16 rows x 64 bytes; here its 16 rows are 4 weight rows x 4
 // segments of 64 bytes (A row m: weight row 4i + (m >> 2), bytes 64 (m & 3) ..
 // of the record's 256), and the B operand's 16 columns are 4 vectors x the
