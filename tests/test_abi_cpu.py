@@ -205,6 +205,21 @@ def test_launch_config_tiles(loom):
     assert loom.launch_config_invoke(t, [63])["workgroup_size"] == (64, 1, 1)
 
 
+def test_one_vector_never_takes_the_matrix_cores(loom):
+    # Every row length with one vector runs a v_dot4 GEMV form: a 64-lane
+    # wave per block of rows with no LDS, or a workgroup per row whose LDS holds
+    # one total per wave.  The matrix-core kernels use 16-row tiles and stage
+    # records or partial tiles in LDS, so neither shape can be taken for theirs.
+    i8 = loom.launch_config_lookup("i8_dequant_dot")
+    rows = 100
+    for k in list(range(0, 40000, 4)) + [65536, 131068, 1 << 20]:
+        cfg = loom.launch_config_invoke(i8, [rows, k, 1])
+        size, lds = cfg["workgroup_size"][0], cfg["workgroup_storage_bytes"]
+        rows_form = size == 64 and lds == 0
+        wide_form = cfg["workgroups"] == (rows, 1, 1) and size % 64 == 0 and lds == 4 * (size // 64)
+        assert rows_form or wide_form, (k, cfg)
+
+
 def test_launch_config_errors(loom, lib):
     with pytest.raises(loom.LoomError) as e:
         loom.launch_config_lookup("no_such_kernel")
