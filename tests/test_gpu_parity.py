@@ -515,6 +515,10 @@ I8_CASES = [
     # 6 vectors on the tile kernel next to it
     (13, 8192, 7), (70, 1024, 7), (33, 256, 7), (8200, 16384, 8), (8193, 16384, 2), (8300, 16384, 4),
     (8210, 16388, 5), (600, 16384, 7), (13, 8192, 6), (8200, 16384, 6),
+    # 8 waves per tile with 3 vectors and a partly empty last record (k a
+    # multiple of 16, not of 256), with 7 vectors at whole records, and one
+    # whole 16-row tile
+    (8197, 20000, 3), (8240, 16640, 7), (16, 8192, 8),
     # 9-16 vectors with k a multiple of 1024 from 4096 to 8192: the row-streaming
     # kernel (one workgroup per CU walking 16-row tiles; 8197 rows give 513
     # tiles, so workgroups take two or three tiles each)
