@@ -568,10 +568,12 @@ def test_i8_unaligned_operands(loom, device, rows, k, batch):
     _check_i8(_np(y), _np(acc), w, x, ws, xs, f"unaligned {rows}x{k}x{batch}")
 
 
-@pytest.mark.parametrize("batch", [1, 8])
+@pytest.mark.parametrize("batch", [1, 2, 8, 16, 64])
 def test_i8_extremes_at_int32_limit(loom, device, batch):
     # k = 131068 with every byte -128: acc = 16384 k = 2^31 - 65536, the largest
     # accumulator the range check admits; the opposite sign on half the vectors
+    # (one vector: the GEMV; 2 and 16: the tile kernel; 8: the segment-paired
+    # kernel; 64: the column-tile kernel)
     k, rows = 131068, 17
     w = torch.full((rows, k), -128, dtype=torch.int8)
     x = torch.full((batch, k), -128, dtype=torch.int8)
