@@ -589,11 +589,13 @@ def test_i8_extremes_at_int32_limit(loom, device, batch):
 
 def test_i8_one_hot_and_byte_order(loom, device):
     # one-hot activations pick single weight columns: pins byte order and
-    # sign extension through the packed words on both kernels
+    # sign extension through the packed words on every kernel (one vector: the
+    # GEMV; 2 and 16: the tile kernel; 8: the segment-paired kernel; 64: the
+    # column-tile kernel)
     rows, k = 24, 256
     w = synth.i8_rows(5, synth.S_W, 0, rows, k)
-    for batch in (1, 8):
-        cols = [3, 64, 129, 255, 0, 17, 18, 19][:batch]
+    for batch in (1, 2, 8, 16, 64):
+        cols = ([3, 64, 129, 255, 0, 17, 18, 19] + [(37 * b + 5) % k for b in range(8, 64)])[:batch]
         x = torch.zeros(batch, k, dtype=torch.int8)
         for b, c in enumerate(cols):
             x[b, c] = 1
